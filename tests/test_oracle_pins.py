@@ -1,0 +1,384 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each check is chosen so that a plausible mistake in the oracle (a dropped term,
+a wrong sign, an off-by-one mask, a transposed operand, a wrong pairing) fails
+at least one of them. None of them re-types an oracle formula or re-calls the
+oracle's own library routine on the same expression.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute, oracle
+from workloads import Dims, make_decode, make_prefill, prefill_recipe
+from workloads.gen import rope_table_bits
+
+TINY = Dims(nope=6, rope=4, v=5, lora=12)
+
+
+# ---------------------------------------------------------------------------
+# storage decoding
+# ---------------------------------------------------------------------------
+
+def test_e4m3fn_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3fn_to_f64(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(nan, [math.isnan(brute.e4m3fn(c)) for c in codes])
+    assert np.array_equal(ref[~nan], np.array([brute.e4m3fn(c) for c in codes])[~nan])
+    # OCP e4m3fn facts: largest finite 448, smallest subnormal 2^-9, no infinity
+    assert np.nanmax(got) == 448.0
+    assert got[1] == 2.0 ** -9
+    assert not np.isinf(got).any()
+
+
+def test_bf16_sample_codes_match_torch():
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 1 << 16, 20000, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    some = bits[:200]
+    assert all(brute.bf16(b) == g or (math.isnan(g)) for b, g in zip(some, got[:200]))
+
+
+# ---------------------------------------------------------------------------
+# plan (mla_prefill_plan page)
+# ---------------------------------------------------------------------------
+
+def test_plan_worked_example_two_sequences():
+    """Hand-worked from the page's Args definitions: lengths 5 (0 cached) and
+    18 (7 cached + 11 new), 8-token chunks, 4 chunk slots."""
+    bro, co, bl = oracle.plan([0, 5, 16], [0, 7], 8, 4)
+    assert bro.tolist() == [[0, 5, 13], [0, 0, 8], [0, 0, 2], [0, 0, 0]]
+    assert co.tolist() == [[0, 0], [5, 8], [5, 16], [5, 18]]
+    assert bl.tolist() == [13, 8, 2, -1]
+    assert bro.dtype == np.uint32 and co.dtype == np.uint32 and bl.dtype == np.int32
+
+
+def _check_invariants(offs, clen, T, C, bro, co, bl):
+    B = len(clen)
+    L = [offs[b + 1] - offs[b] + clen[b] for b in range(B)]
+    used = [c for c in range(C) if bl[c] != -1]
+    # -1 only after the last used chunk
+    if used:
+        assert used == list(range(len(used)))
+    for c in range(C):
+        row = [int(x) for x in bro[c]]
+        assert row[0] == 0
+        assert all(row[i] <= row[i + 1] for i in range(B))  # monotone over b
+        if bl[c] != -1:
+            assert bl[c] == row[B] > 0
+        else:
+            assert row[B] == 0
+    for b in range(B):
+        covered = []
+        for c in range(C):
+            n = int(bro[c, b + 1]) - int(bro[c, b])
+            assert n <= T
+            covered.extend(range(int(co[c, b]), int(co[c, b]) + n))
+            if c:
+                assert co[c, b] >= co[c - 1, b]  # monotone over chunks
+        assert covered == list(range(L[b]))  # every token exactly once, in order
+
+
+def test_plan_closed_form_equals_token_walk_exhaustive():
+    for B in (1, 2):
+        for lens in itertools.product(range(0, 7), repeat=2 * B):
+            new, cached = lens[:B], lens[B:]
+            offs = [0]
+            for n in new:
+                offs.append(offs[-1] + n)
+            for T in range(1, 6):
+                C = max(1, (max(a + b for a, b in zip(new, cached)) + T - 1) // T) + 1
+                bro, co, bl = oracle.plan(offs, cached, T, C)
+                wbro, wco, wbl = brute.plan_walk(offs, cached, T, C)
+                assert bro.tolist() == wbro and co.tolist() == wco and bl.tolist() == wbl
+                _check_invariants(offs, cached, T, C, bro, co, bl)
+
+
+def test_plan_random_batches_invariants_and_walk():
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        B = int(rng.integers(1, 9))
+        new = rng.integers(0, 40, B)
+        cached = rng.integers(0, 60, B)
+        offs = np.concatenate([[0], np.cumsum(new)]).astype(np.uint32)
+        T = int(rng.integers(1, 33))
+        need = max(1, int(((new + cached).max() + T - 1) // T))
+        C = need + int(rng.integers(0, 3))
+        bro, co, bl = oracle.plan(offs, cached, T, C)
+        wbro, wco, wbl = brute.plan_walk(offs, cached, T, C)
+        assert bro.tolist() == wbro and co.tolist() == wco and bl.tolist() == wbl
+        _check_invariants([int(x) for x in offs], [int(x) for x in cached], T, C, bro, co, bl)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and RoPE
+# ---------------------------------------------------------------------------
+
+def test_rms_norm_unit_rms_scale_invariance_and_torch():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((7, 512))
+    y = oracle.rms_norm(x, np.ones(512), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-13)
+    assert np.allclose(oracle.rms_norm(3.5 * x, np.ones(512), 0.0), y, rtol=1e-13)
+    g = 1 + 0.1 * rng.standard_normal(512)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (512,), torch.from_numpy(g),
+                                       eps=1e-6).numpy()
+    assert np.allclose(oracle.rms_norm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-14)
+
+
+def _exact_table(positions, rope):
+    i = np.arange(rope // 2)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * 10000.0 ** (-2.0 * i / rope)
+    t = np.empty((len(positions), rope))
+    t[:, 0::2] = np.cos(ang)
+    t[:, 1::2] = np.sin(ang)
+    return t
+
+
+def test_rope_identity_norm_composition_and_complex_multiply():
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal((5, 64))
+    # position 0: the stored table row is (1, 0, 1, 0, ...) exactly
+    f0 = oracle.bf16_to_f64(rope_table_bits(1, 64))
+    assert np.array_equal(f0[0], np.tile([1.0, 0.0], 32))
+    assert np.array_equal(oracle.rope(y, np.repeat(f0, 5, axis=0)), y)
+    # pair norms preserved
+    F = _exact_table([3, 17, 100, 2000, 4095], 64)
+    r = oracle.rope(y, F)
+    assert np.allclose(np.hypot(r[:, 0::2], r[:, 1::2]), np.hypot(y[:, 0::2], y[:, 1::2]),
+                       rtol=1e-13)
+    # R(p1) R(p2) = R(p1 + p2)
+    p1, p2 = np.array([5, 9, 300, 1000, 7]), np.array([2, 40, 11, 77, 4000])
+    two = oracle.rope(oracle.rope(y, _exact_table(p1, 64)), _exact_table(p2, 64))
+    assert np.allclose(two, oracle.rope(y, _exact_table(p1 + p2, 64)), rtol=1e-9, atol=1e-11)
+    # complex multiply of adjacent pairs by cis
+    yc = torch.view_as_complex(torch.from_numpy(y).reshape(5, 32, 2).contiguous())
+    fc = torch.view_as_complex(torch.from_numpy(F).reshape(5, 32, 2).contiguous())
+    ref = torch.view_as_real(yc * fc).reshape(5, 64).numpy()
+    assert np.allclose(r, ref, rtol=1e-13, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# the two tiers against each other, on tiny inputs
+# ---------------------------------------------------------------------------
+
+def _tiny_prefill(seed, new, cached, H=3, ps=4, T=3, fp8=False, dims=TINY):
+    return make_prefill("tiny", seed, new, cached, H, ps, T, fp8=fp8, dims=dims)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_brute_equals_oracle_prefill_tiny_dims(fp8):
+    wl = _tiny_prefill(7, [3, 0, 6, 1], [2, 4, 0, 9], fp8=fp8)
+    ref = np.array(brute.prefill(wl))
+    got = oracle.prefill(wl)
+    assert ref.shape == got.shape
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_brute_equals_oracle_decode_tiny_dims():
+    for fp8 in (False, True):
+        wl = make_decode("tinyd", 3, [1, 5, 9], 3, 4, fp8=fp8, dims=TINY)
+        assert np.allclose(oracle.decode(wl), np.array(brute.decode(wl)), rtol=1e-12, atol=1e-13)
+
+
+def test_brute_equals_oracle_prefill_two_sequence_batch_full_dims():
+    wl = prefill_recipe("tiny_b2")
+    ref = np.array(brute.prefill(wl))
+    got = oracle.prefill(wl)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# attention closed forms and library references
+# ---------------------------------------------------------------------------
+
+def _with_q(wl, qvals):
+    from workloads import f32_to_bf16_bits
+    wl.q = f32_to_bf16_bits(np.asarray(qvals, dtype=np.float32))
+    return wl
+
+
+def test_single_visible_key_returns_its_value():
+    wl = _tiny_prefill(3, [4], [0])
+    dec = oracle.Decoded(wl)
+    out = oracle.prefill(wl, dec)
+    latn, _ = dec.seq_keys(0)
+    _, v = oracle.up_project(latn, dec.w_k, dec.w_uv, dec.H)
+    assert np.allclose(out[0], v[0], rtol=1e-13, atol=1e-14)  # query 0 sees key 0 only
+
+
+def test_zero_query_gives_prefix_mean_of_values():
+    wl = _tiny_prefill(4, [5, 3], [2, 0])
+    wl = _with_q(wl, np.zeros(wl.q.shape))
+    dec = oracle.Decoded(wl)
+    out = oracle.prefill(wl, dec)
+    for b in range(2):
+        latn, _ = dec.seq_keys(b)
+        _, v = oracle.up_project(latn, dec.w_k, dec.w_uv, dec.H)
+        for i in range(dec.offs[b + 1] - dec.offs[b]):
+            P = dec.clen[b] + i
+            assert np.allclose(out[dec.offs[b] + i], v[:P + 1].mean(axis=0), rtol=1e-12)
+
+
+def test_softmax_weights_sum_to_one_constant_values():
+    """With every value row equal to the same vector, each output equals it."""
+    rng = np.random.default_rng(5)
+    n, L, H = 6, 9, 3
+    q = rng.standard_normal((n, H, 10))
+    k_nope = rng.standard_normal((L, H, 6))
+    krope = rng.standard_normal((L, 4))
+    const = rng.standard_normal(5)
+    v = np.broadcast_to(const, (L, H, 5)).copy()
+    out = oracle.attend_sequence(q, k_nope, krope, v, 3 + np.arange(n), np.arange(L), 0.4, 6)
+    assert np.allclose(out, np.broadcast_to(const, out.shape), rtol=1e-13, atol=1e-14)
+    # and every output is a convex combination of the visible values
+    v = rng.standard_normal((L, H, 5))
+    out = oracle.attend_sequence(q, k_nope, krope, v, 3 + np.arange(n), np.arange(L), 0.4, 6)
+    for i in range(n):
+        vis = v[:3 + i + 1]
+        assert (out[i] <= vis.max(axis=0) + 1e-12).all() and (out[i] >= vis.min(axis=0) - 1e-12).all()
+
+
+def test_matches_torch_sdpa_with_bottom_right_mask():
+    wl = _tiny_prefill(6, [5, 7], [4, 0], H=2)
+    dec = oracle.Decoded(wl)
+    out = oracle.prefill(wl, dec)
+    for b in range(2):
+        n = dec.offs[b + 1] - dec.offs[b]
+        latn, krope = dec.seq_keys(b)
+        k_nope, v = oracle.up_project(latn, dec.w_k, dec.w_uv, dec.H)
+        L = latn.shape[0]
+        K = np.concatenate([k_nope, np.broadcast_to(krope[:, None, :], (L, dec.H, dec.rope))], -1)
+        q = torch.from_numpy(dec.q[dec.offs[b]:dec.offs[b + 1]]).permute(1, 0, 2)
+        k = torch.from_numpy(K).permute(1, 0, 2)
+        vv = torch.from_numpy(np.ascontiguousarray(v)).permute(1, 0, 2)
+        # bottom-right aligned causal mask: the last query sees every key
+        mask = torch.ones(n, L, dtype=torch.bool).tril(diagonal=L - n)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, k, vv, attn_mask=mask, scale=wl.scale).permute(1, 0, 2).numpy()
+        assert np.allclose(out[dec.offs[b]:dec.offs[b + 1]], ref, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 1000])
+def test_chunk_size_invariance(T):
+    wl = _tiny_prefill(8, [5, 9, 2], [6, 0, 11])
+    ref = oracle.prefill(wl)
+    got, (bro, co, bl) = oracle.prefill_chunked(wl, buffer_token_size=T)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_page_permutation_invariance():
+    wl = _tiny_prefill(9, [4, 6], [7, 3], ps=2)
+    ref = oracle.prefill(wl)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(wl.num_pages)  # new position of each old page
+    pool = np.empty_like(wl.pool)
+    pool[perm] = wl.pool
+    wl.pool = pool
+    wl.page_table = perm[wl.page_table].astype(np.int32)
+    assert np.allclose(oracle.prefill(wl), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_sampled_rows_equal_full_output():
+    wl = _tiny_prefill(10, [7, 4], [3, 9])
+    full = oracle.prefill(wl)
+    samples = [(0, 0), (3, 2), (6, 1), (8, 0), (10, 2)]
+    got = oracle.prefill_sampled(wl, samples)
+    for i, (t, h) in enumerate(samples):
+        assert np.allclose(got[i], full[t, h], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# decode: absorbed form against the up-projected form, splits, SDPA-MQA
+# ---------------------------------------------------------------------------
+
+def _decode_from_prefill(wl):
+    """Decode workload whose rows are the processed prefill keys, w_uk taken from w_k."""
+    from workloads import DecodeWorkload
+    dec = oracle.Decoded(wl)
+    d = wl.dims
+    rows = np.zeros((wl.num_pages * wl.page_size, d.cache_depth))
+    for b in range(dec.B):
+        latn, krope = dec.seq_keys(b)
+        p = np.arange(latn.shape[0])
+        slot = wl.page_table[b, p // wl.page_size].astype(np.int64) * wl.page_size \
+            + p % wl.page_size
+        rows[slot, :d.lora] = latn
+        rows[slot, d.lora:] = krope
+    w_uk = wl.w_k.reshape(wl.num_heads, d.nope, d.lora).transpose(0, 2, 1).copy()
+    last = [int(x) - 1 for x in wl.input_row_offsets[1:]]
+    dwl = DecodeWorkload(name="equiv", seed=0, dims=d, num_heads=wl.num_heads,
+                         page_size=wl.page_size, fp8=False,
+                         context_lens=wl.seq_lens.astype(np.uint32),
+                         page_table=wl.page_table, pool=None, q=wl.q[last], w_uk=w_uk,
+                         w_uv=wl.w_uv, scale=wl.scale)
+    return dwl, rows.reshape(wl.num_pages, wl.page_size, d.cache_depth), last
+
+
+def test_absorbed_decode_equals_up_projected_prefill():
+    wl = _tiny_prefill(12, [3, 5, 2], [4, 0, 6], H=4)
+    ref = oracle.prefill(wl)
+    dwl, rows, last = _decode_from_prefill(wl)
+    ddec = oracle.DecodedDecode.__new__(oracle.DecodedDecode)
+    d = wl.dims
+    ddec.wl, ddec.nope, ddec.rope, ddec.v, ddec.lora = dwl, d.nope, d.rope, d.v, d.lora
+    ddec.H = wl.num_heads
+    ddec.q = oracle.bf16_to_f64(dwl.q)
+    ddec.pool = rows
+    ddec.w_uk = oracle.bf16_to_f64(dwl.w_uk)
+    ddec.w_uv = oracle.bf16_to_f64(dwl.w_uv)
+    ddec.ctx = [int(x) for x in dwl.context_lens]
+    got = oracle.decode(dwl, ddec)
+    assert np.allclose(got, ref[last], rtol=1e-10, atol=1e-12)
+
+
+def test_absorbed_decode_equals_up_projected_prefill_full_dims():
+    wl = prefill_recipe("tiny_b2")
+    ref = oracle.prefill(wl)
+    dwl, rows, last = _decode_from_prefill(wl)
+    ddec = oracle.DecodedDecode.__new__(oracle.DecodedDecode)
+    d = wl.dims
+    ddec.wl, ddec.nope, ddec.rope, ddec.v, ddec.lora = dwl, d.nope, d.rope, d.v, d.lora
+    ddec.H = wl.num_heads
+    ddec.q = oracle.bf16_to_f64(dwl.q)
+    ddec.pool = rows
+    ddec.w_uk = oracle.bf16_to_f64(dwl.w_uk)
+    ddec.w_uv = oracle.bf16_to_f64(dwl.w_uv)
+    ddec.ctx = [int(x) for x in dwl.context_lens]
+    got = oracle.decode(dwl, ddec)
+    assert np.allclose(got, ref[last], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 16])
+def test_decode_split_invariance(splits):
+    wl = make_decode("tinyd", 13, [1, 7, 30, 16], 3, 4, dims=TINY)
+    assert np.allclose(oracle.decode_split(wl, splits), oracle.decode(wl), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_matches_torch_sdpa_single_kv_head():
+    wl = make_decode("tinyd", 14, [9, 3], 4, 4, dims=TINY)
+    dec = oracle.DecodedDecode(wl)
+    out = oracle.decode(wl, dec)
+    d = wl.dims
+    for b in range(2):
+        Z = oracle.gather_rows(dec.pool, wl.page_table, b, np.arange(dec.ctx[b]), wl.page_size)
+        # up-projected multi-head form: per head, K = [Z_lat @ w_uk[h] | Z_rope],
+        # V = Z_lat @ w_uv[h]^T
+        for h in range(dec.H):
+            K = np.concatenate([Z[:, :d.lora] @ dec.w_uk[h], Z[:, d.lora:]], axis=1)
+            V = Z[:, :d.lora] @ dec.w_uv[h].T
+            q = torch.from_numpy(dec.q[b, h][None, None, :])
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, torch.from_numpy(K)[None], torch.from_numpy(V)[None], scale=wl.scale)
+            assert np.allclose(out[b, h], ref[0, 0].numpy(), rtol=1e-11, atol=1e-13)
