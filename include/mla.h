@@ -1,0 +1,283 @@
+/*
+ * mla.h -- C ABI of libmla.so: MLA chunked prefill and absorbed decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow three Modular MAX kernel-library API pages:
+ *   "mla_prefill_plan"              (chunk planner: description and Args),
+ *   "mla_prefill_decode_graph_bf16" (latent gather, RMSNorm, RoPE,
+ *                                    up-projection with w_k / w_uv, absorbed
+ *                                    decode with w_uk / w_uv: description,
+ *                                    Parameters and Args),
+ *   "flare_mla_prefill_dispatch"    (prefill attention: q_depth 192 = 128 nope
+ *                                    + 64 rope, one rope head shared by all
+ *                                    query heads, cache_depth 576, bf16 or
+ *                                    float8_e4m3fn inputs with bf16 output).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Dimensions are fixed to DeepSeek V2/V3 MLA: qk_nope 128, qk_rope 64,
+ *   v_head 128, kv_lora_rank 512, cache row 576 = 512 latent + 64 rope.
+ *   num_heads is a runtime argument (1..1024).
+ * - Every pointer argument is a DEVICE pointer owned by the caller (for
+ *   example memory allocated through torch). The library never allocates,
+ *   frees or keeps device memory; scratch space comes from a caller-provided
+ *   workspace whose size the matching *_workspace_size function returns.
+ * - Every call is asynchronous on the caller's stream and never synchronises
+ *   the host, so a sequence of calls can be captured into a HIP graph.
+ *   Device-resident plan values (buffer_lengths) are read on the device.
+ * - All tensors are dense, row-major and contiguous in the shapes given.
+ *   "bf16" is bfloat16, "e4m3" is OCP float8_e4m3fn (1-4-3, bias 7, no
+ *   infinities), each passed as raw storage.
+ * - Every function returns MLA_OK (0) or a negative status. Host-checkable
+ *   problems (null pointers, sizes out of range, unsupported dtypes, a
+ *   workspace that is too small) are reported before anything is enqueued.
+ *   Data-dependent preconditions on device values (page ids inside the pool,
+ *   positions inside the RoPE table, max_chunks large enough for the batch)
+ *   cannot be checked without a synchronisation: kernels clamp or skip
+ *   offending rows so that they never read out of bounds, and the results for
+ *   such rows are unspecified.
+ *   mla_last_error() returns a message for the last failure on the calling
+ *   thread.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MLA_OK 0
+#define MLA_ERR_INVALID_ARG (-1) /* null pointer, size out of range           */
+#define MLA_ERR_UNSUPPORTED (-2) /* dtype other than bf16 / e4m3 where allowed */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace pointer null or too small        */
+#define MLA_ERR_HIP (-4)         /* a kernel launch failed                     */
+
+/* storage dtypes */
+#define MLA_BF16 0
+#define MLA_FP8_E4M3FN 1
+
+/* fixed MLA dimensions */
+#define MLA_QK_NOPE 128
+#define MLA_QK_ROPE 64
+#define MLA_Q_DEPTH 192
+#define MLA_V_DEPTH 128
+#define MLA_KV_LORA 512
+#define MLA_CACHE_DEPTH 576
+
+/*
+ * mla_prefill_plan -- split every sequence's cached-plus-new tokens into
+ * chunks of at most buffer_token_size tokens per sequence
+ * ("mla_prefill_plan" page, description and Args).
+ *
+ * Sequence b holds L_b = (input_row_offsets[b+1] - input_row_offsets[b]) +
+ * cache_lengths[b] tokens, cached ones first. Chunk c takes
+ *   len(c, b) = clamp(L_b - c*T, 0, T) tokens starting at position
+ *   cache_offsets[c, b] = min(c*T, L_b),
+ * packed sequence after sequence in the chunk's contiguous buffer:
+ *   buffer_row_offsets[c, 0] = 0, buffer_row_offsets[c, b+1] =
+ *   buffer_row_offsets[c, b] + len(c, b),
+ *   buffer_lengths[c] = buffer_row_offsets[c, B], or -1 when that is 0
+ *   (an unused chunk). Every element of every chunk row is written.
+ *
+ * Outputs (device):
+ *   buffer_row_offsets  uint32 [max_chunks, batch_size + 1]
+ *   cache_offsets       uint32 [max_chunks, batch_size]
+ *   buffer_lengths      int32  [max_chunks]
+ *   chunks_needed       uint32 [1] or NULL: ceil(max_b L_b / T), so the caller
+ *                       can check later that max_chunks was large enough.
+ * Inputs (device):
+ *   input_row_offsets   uint32 [batch_size + 1], cumulative new-token offsets
+ *   cache_lengths       uint32 [batch_size], cached tokens per sequence
+ * Host scalars: batch_size >= 1, max_chunks >= 1, buffer_token_size >= 1,
+ *   batch_size * buffer_token_size < 2^31.
+ */
+int mla_prefill_plan(uint32_t* buffer_row_offsets, uint32_t* cache_offsets,
+                     int32_t* buffer_lengths, uint32_t* chunks_needed,
+                     const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                     int32_t batch_size, int32_t max_chunks, uint32_t buffer_token_size,
+                     hipStream_t stream);
+
+/*
+ * mla_gather_norm_rope -- gather one chunk's raw cache rows from the paged
+ * pool, RMSNorm the 512-wide latent with kv_norm_gamma and rotate the 64-wide
+ * rope part with freqs_cis ("mla_prefill_decode_graph_bf16" page: Parameters
+ * "kv_input_fn"; Args "kv_norm_gamma", "epsilon", "freqs_cis",
+ * "buffer_row_offsets", "cache_offsets").
+ *
+ * For every row r < *buffer_length_c of sequence b (buffer_row_offsets_c[b]
+ * <= r < buffer_row_offsets_c[b+1]) at position p = cache_offsets_c[b] +
+ * (r - buffer_row_offsets_c[b]), the pool row is
+ *   kv_cache[page_table[b, p / page_size], p % page_size, :]   (576 values)
+ *   latent_out[r, l] = x_l * gamma_l / sqrt(mean(x^2) + epsilon), x = row[0:512]
+ *   krope_out[r, 2i]   = y_2i F_2i - y_2i+1 F_2i+1,   y = row[512:576],
+ *   krope_out[r, 2i+1] = y_2i F_2i+1 + y_2i+1 F_2i,   F = freqs_cis[p, :].
+ * Arithmetic is fp32; outputs are rounded to bf16 (krope to e4m3 when
+ * krope_dtype is MLA_FP8_E4M3FN, saturating at 448).
+ *
+ *   latent_out    bf16 [max_rows, 512]           (device, written)
+ *   krope_out     bf16 or e4m3 [max_rows, 64]    (device, written)
+ *   kv_cache      bf16 or e4m3 [num_pages, page_size, 576] (cache_dtype)
+ *   page_table    int32 [batch_size, max_pages_per_seq]
+ *   buffer_row_offsets_c uint32 [batch_size + 1]  one chunk's plan row
+ *   cache_offsets_c      uint32 [batch_size]
+ *   buffer_length_c      int32 [1]  rows in this chunk; -1 makes the call a no-op
+ *   kv_norm_gamma bf16 [512];  freqs_cis bf16 [max_seq_len, 64]
+ * Rows whose page id or position is out of range are written as zeros.
+ */
+int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
+                         const void* kv_cache, int32_t cache_dtype,
+                         const int32_t* page_table,
+                         const uint32_t* buffer_row_offsets_c,
+                         const uint32_t* cache_offsets_c,
+                         const int32_t* buffer_length_c,
+                         const void* kv_norm_gamma, const void* freqs_cis,
+                         int32_t batch_size, int32_t page_size, int32_t max_pages_per_seq,
+                         int32_t num_pages, int32_t max_rows, int32_t max_seq_len,
+                         float epsilon, hipStream_t stream);
+
+/*
+ * mla_up_project -- K_nope and V from the normalised latent
+ * ("mla_prefill_decode_graph_bf16" page, Args "w_k" and "w_uv"):
+ *   K_nope[r, h, d] = sum_l w_k[h*128 + d, l] latent[r, l]
+ *   V[r, h, d]      = sum_l w_uv[h, d, l]     latent[r, l]
+ * for r < *buffer_length_c; bf16 MFMA with fp32 accumulation.
+ *
+ * Output layouts are the ones the attention kernel streams:
+ *   k_nope_out  [num_heads, max_rows, 128], bf16 or e4m3 (k_dtype)
+ *   v_t_out     [num_heads, 128, max_rows], bf16: V transposed per head
+ * Inputs: latent bf16 [max_rows, 512]; w_k bf16 [num_heads*128, 512];
+ *   w_uv bf16 [num_heads, 128, 512]; buffer_length_c int32 [1] (-1: no-op).
+ * max_rows must be a multiple of 64 (the row stride of both outputs).
+ */
+int mla_up_project(void* k_nope_out, void* v_t_out, int32_t k_dtype,
+                   const void* latent, const void* w_k, const void* w_uv,
+                   const int32_t* buffer_length_c, int32_t num_heads, int32_t max_rows,
+                   hipStream_t stream);
+
+/*
+ * mla_prefill_attention_workspace_size / mla_prefill_attention -- one chunk of
+ * causal MLA prefill attention ("flare_mla_prefill_dispatch" page: Args q,
+ * k, v, k_rope, valid_length, max_prompt_len, scale, cache_offsets;
+ * Parameters kv_num_heads = 1 for the rope part, q_depth 192).
+ *
+ * Query i of sequence b (token t = input_row_offsets[b] + i) sits at absolute
+ * position P = cache_lengths[b] + i and sees the keys of this chunk at
+ * positions p = cache_offsets_c[b] + j <= P, j < len(b). Its score is
+ *   s = scale * (q[t, h, 0:128] . K_nope[r, h, :] + q[t, h, 128:192] . krope[r, :])
+ * with r = buffer_row_offsets_c[b] + j; krope has one head shared by all query
+ * heads. Softmax state (running max, sum, unnormalised output) is carried
+ * across the chunks of a sequence in the workspace; a query's output
+ *   output[t, h, :] = sum_p softmax(s)_p V[p, h, :]
+ * is written (bf16) in the chunk that holds its last visible key. Chunks must
+ * be issued in order and each sequence's keys must appear in increasing,
+ * contiguous position ranges, as mla_prefill_plan produces them.
+ *
+ *   output   bf16 [total_q, num_heads, 128]                  (written)
+ *   q        bf16 or e4m3 (dtype) [total_q, num_heads, 192]  nope first
+ *   k_nope   [num_heads, max_rows, 128]  bf16, or e4m3 when dtype is e4m3
+ *   v_t      bf16 [num_heads, 128, max_rows]
+ *   krope    [max_rows, 64]  bf16, or e4m3 when dtype is e4m3
+ *   input_row_offsets uint32 [B+1]; cache_lengths uint32 [B]
+ *   buffer_row_offsets_c uint32 [B+1]; cache_offsets_c uint32 [B];
+ *   buffer_length_c int32 [1] (-1: no-op)
+ *   max_prompt_len: host upper bound on the new tokens of any sequence
+ *   workspace: mla_prefill_attention_workspace_size(...) bytes, holding the
+ *   carried softmax state and the query-block schedule. A sequence's carry is
+ *   read only when cache_offsets_c[b] > 0, i.e. when earlier chunks held its
+ *   first keys, so no reset is needed between prefills.
+ */
+size_t mla_prefill_attention_workspace_size(int32_t batch_size, int32_t total_q,
+                                            int32_t num_heads);
+int mla_prefill_attention(void* output, const void* q, int32_t dtype,
+                          const void* k_nope, const void* v_t, const void* krope,
+                          const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                          const uint32_t* buffer_row_offsets_c,
+                          const uint32_t* cache_offsets_c,
+                          const int32_t* buffer_length_c,
+                          int32_t batch_size, int32_t total_q, int32_t num_heads,
+                          int32_t max_rows, int32_t max_prompt_len, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_prefill_workspace_size / mla_prefill -- the whole chunked prefill for a
+ * planned batch: for every chunk c < max_chunks (in order) gather + RMSNorm +
+ * RoPE, up-projection, and attention with the carried softmax state
+ * ("mla_prefill_decode_graph_bf16" page, prefill branch, called once per
+ * chunk with that chunk's plan row). Chunks with buffer_lengths[c] == -1 are
+ * skipped on the device.
+ *
+ *   output        bf16 [total_q, num_heads, 128]
+ *   q             bf16 or e4m3 (dtype) [total_q, num_heads, 192]
+ *   kv_cache      [num_pages, page_size, 576] raw latent + raw rope rows,
+ *                 same dtype as q
+ *   page_table    int32 [batch_size, max_pages_per_seq]
+ *   buffer_row_offsets uint32 [max_chunks, B+1]; cache_offsets uint32
+ *                 [max_chunks, B]; buffer_lengths int32 [max_chunks]  (the plan)
+ *   w_k bf16 [num_heads*128, 512]; w_uv bf16 [num_heads, 128, 512]
+ *   kv_norm_gamma bf16 [512]; freqs_cis bf16 [max_seq_len, 64]
+ *   max_rows: host upper bound on every buffer_lengths[c] (B * T always is)
+ * With dtype MLA_FP8_E4M3FN the scores are computed from e4m3 q, K_nope and
+ * krope on fp8 MFMA, and the value product in bf16.
+ */
+size_t mla_prefill_workspace_size(int32_t batch_size, int32_t total_q, int32_t num_heads,
+                                  int32_t max_rows, int32_t dtype);
+int mla_prefill(void* output, const void* q, int32_t dtype,
+                const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                const void* kv_cache, const int32_t* page_table,
+                const uint32_t* buffer_row_offsets, const uint32_t* cache_offsets,
+                const int32_t* buffer_lengths, int32_t max_chunks, int32_t max_rows,
+                const void* w_k, const void* w_uv, const void* kv_norm_gamma,
+                const void* freqs_cis, int32_t batch_size, int32_t total_q,
+                int32_t num_heads, int32_t max_prompt_len, int32_t page_size,
+                int32_t max_pages_per_seq, int32_t num_pages, int32_t max_seq_len,
+                float scale, float epsilon, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * mla_decode_workspace_size / mla_decode -- absorbed MLA decode, one new token
+ * per sequence ("mla_prefill_decode_graph_bf16" page, decode branch and Args
+ * "w_uk", "w_uv"; "flare_mla_prefill_dispatch" page: kv_num_heads 1,
+ * cache_depth 576):
+ *   q_lat[b, h, :] = w_uk[h] (512x128) . q[b, h, 0:128]
+ *   s_p = scale * (q_lat . Z_p[0:512] + q[b, h, 128:192] . Z_p[512:576])
+ *   o_lat = sum_p softmax(s)_p Z_p[0:512];  output[b, h, :] = w_uv[h] (128x512) . o_lat
+ * over the rows Z_p, p < context_lengths[b], of sequence b as stored in the
+ * pool (already normalised and rotated). The context is cut into split-KV
+ * partitions whose partial states are merged by log-sum-exp;
+ * num_partitions = 0 lets the library choose.
+ *
+ *   output     bf16 [batch_size, num_heads, 128]
+ *   q          bf16 [batch_size, num_heads, 192]
+ *   context_lengths uint32 [batch_size]  (>= 1, includes the new token)
+ *   kv_cache   bf16 or e4m3 (cache_dtype) [num_pages, page_size, 576]
+ *   page_table int32 [batch_size, max_pages_per_seq]
+ *   w_uk bf16 [num_heads, 512, 128]; w_uv bf16 [num_heads, 128, 512]
+ *   max_context_len: host upper bound on every context length
+ * With an e4m3 cache both products run on fp8 MFMA (q_lat and the softmax
+ * weights are rounded to e4m3).
+ */
+size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads,
+                                 int32_t max_context_len, int32_t num_partitions,
+                                 int32_t cache_dtype);
+int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
+               const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+               const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
+               int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+               int32_t max_context_len, int32_t num_partitions, float scale,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text for a status code, and the message of the calling thread's last failure. */
+const char* mla_status_string(int status);
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

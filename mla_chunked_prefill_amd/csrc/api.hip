@@ -1,0 +1,411 @@
+// C ABI of libmla.so: host-side validation, workspace layout and kernel
+// launches. Declarations and contracts are in include/mla.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <stdarg.h>
+
+#include "../../include/mla.h"
+#include "kernels.hpp"
+
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLA_OK;
+  return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(int32_t d) { return d == MLA_BF16 || d == MLA_FP8_E4M3FN; }
+size_t dsize(int32_t d) { return d == MLA_FP8_E4M3FN ? 1 : 2; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// prefill-attention workspace: carry O [Tq][H][128] f32, carry ml [Tq][H][2] f32,
+// schedule [n_slots] int2
+struct AttnWs {
+  float* carry_o;
+  float* carry_ml;
+  int2* sched;
+  size_t bytes;
+};
+AttnWs attn_ws_layout(char* base, int B, int total_q, int H) {
+  AttnWs w;
+  size_t off = 0;
+  w.carry_o = (float*)(base + off);
+  off = align_up(off + (size_t)total_q * H * mla::kV * sizeof(float));
+  w.carry_ml = (float*)(base + off);
+  off = align_up(off + (size_t)total_q * H * 2 * sizeof(float));
+  w.sched = (int2*)(base + off);
+  off = align_up(off + (size_t)mla::attn_num_slots(B, total_q) * sizeof(int2));
+  w.bytes = off;
+  return w;
+}
+
+// prefill workspace: latent [R][512] bf16, krope [R][64], K_nope [H][R][128],
+// V^T [H][128][R] bf16, then the attention workspace
+struct PrefillWs {
+  uint16_t* latn;
+  void* krope;
+  void* k_nope;
+  uint16_t* v_t;
+  AttnWs attn;
+  size_t bytes;
+};
+PrefillWs prefill_ws_layout(char* base, int B, int total_q, int H, int max_rows, int dtype) {
+  PrefillWs w;
+  size_t off = 0;
+  const size_t R = (size_t)max_rows;
+  w.latn = (uint16_t*)(base + off);
+  off = align_up(off + R * mla::kLora * 2);
+  w.krope = base + off;
+  off = align_up(off + R * mla::kRope * dsize(dtype));
+  w.k_nope = base + off;
+  off = align_up(off + (size_t)H * R * mla::kNope * dsize(dtype));
+  w.v_t = (uint16_t*)(base + off);
+  off = align_up(off + (size_t)H * mla::kV * R * 2);
+  w.attn = attn_ws_layout(base ? base + off : nullptr, B, total_q, H);
+  off += w.attn.bytes;
+  w.bytes = off;
+  return w;
+}
+
+// decode workspace: q_abs [B][H][576], part_o [B][P][H][512] f32,
+// part_ml [B][P][H][2] f32, o_lat [B][H][512] bf16
+constexpr int kDefaultKeysPerPart = 2048;
+
+int choose_keys_per_part(int B, int max_ctx, int num_partitions) {
+  if (num_partitions > 0) {
+    int kpp = (max_ctx + num_partitions - 1) / num_partitions;
+    kpp = (kpp + 31) / 32 * 32;  // whole key tiles
+    return kpp < 32 ? 32 : kpp;
+  }
+  (void)B;
+  return kDefaultKeysPerPart;
+}
+
+struct DecodeWs {
+  void* q_abs;
+  float* part_o;
+  float* part_ml;
+  uint16_t* o_lat;
+  int P, kpp;
+  size_t bytes;
+};
+DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int num_partitions,
+                          int cache_dtype) {
+  DecodeWs w;
+  w.kpp = choose_keys_per_part(B, max_ctx, num_partitions);
+  w.P = (max_ctx + w.kpp - 1) / w.kpp;
+  size_t off = 0;
+  w.q_abs = base + off;
+  off = align_up(off + (size_t)B * H * mla::kCache * dsize(cache_dtype));
+  w.part_o = (float*)(base + off);
+  off = align_up(off + (size_t)B * w.P * H * mla::kLora * sizeof(float));
+  w.part_ml = (float*)(base + off);
+  off = align_up(off + (size_t)B * w.P * H * 2 * sizeof(float));
+  w.o_lat = (uint16_t*)(base + off);
+  off = align_up(off + (size_t)B * H * mla::kLora * 2);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dtype or dimension";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error; }
+
+int mla_prefill_plan(uint32_t* buffer_row_offsets, uint32_t* cache_offsets,
+                     int32_t* buffer_lengths, uint32_t* chunks_needed,
+                     const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                     int32_t batch_size, int32_t max_chunks, uint32_t buffer_token_size,
+                     hipStream_t stream) {
+  if (!buffer_row_offsets || !cache_offsets || !buffer_lengths || !input_row_offsets ||
+      !cache_lengths)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_plan: null pointer");
+  if (batch_size < 1 || max_chunks < 1 || buffer_token_size < 1)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_plan: batch_size=%d max_chunks=%d T=%u",
+                batch_size, max_chunks, buffer_token_size);
+  if ((uint64_t)batch_size * buffer_token_size >= (1ull << 31))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_plan: batch_size * T must be < 2^31");
+  return hip_status(mla::launch_plan(buffer_row_offsets, cache_offsets, buffer_lengths,
+                                     chunks_needed, input_row_offsets, cache_lengths,
+                                     batch_size, max_chunks, buffer_token_size, stream),
+                    "plan kernel");
+}
+
+int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
+                         const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                         const uint32_t* buffer_row_offsets_c, const uint32_t* cache_offsets_c,
+                         const int32_t* buffer_length_c, const void* kv_norm_gamma,
+                         const void* freqs_cis, int32_t batch_size, int32_t page_size,
+                         int32_t max_pages_per_seq, int32_t num_pages, int32_t max_rows,
+                         int32_t max_seq_len, float epsilon, hipStream_t stream) {
+  if (!latent_out || !krope_out || !kv_cache || !page_table || !buffer_row_offsets_c ||
+      !cache_offsets_c || !buffer_length_c || !kv_norm_gamma || !freqs_cis)
+    return fail(MLA_ERR_INVALID_ARG, "mla_gather_norm_rope: null pointer");
+  if (!dtype_ok(krope_dtype) || !dtype_ok(cache_dtype))
+    return fail(MLA_ERR_UNSUPPORTED, "mla_gather_norm_rope: dtype");
+  if (batch_size < 1 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+      max_rows < 1 || max_seq_len < 1 || !(epsilon >= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_gather_norm_rope: sizes");
+  mla::GatherArgs a;
+  a.latn = (uint16_t*)latent_out;
+  a.krope = krope_out;
+  a.cache = kv_cache;
+  a.page_table = page_table;
+  a.bro_c = buffer_row_offsets_c;
+  a.co_c = cache_offsets_c;
+  a.bl_c = buffer_length_c;
+  a.gamma = (const uint16_t*)kv_norm_gamma;
+  a.freqs = (const uint16_t*)freqs_cis;
+  a.B = batch_size;
+  a.ps = page_size;
+  a.maxp = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.max_rows = max_rows;
+  a.max_seq_len = max_seq_len;
+  a.eps = epsilon;
+  return hip_status(mla::launch_gather(a, cache_dtype == MLA_FP8_E4M3FN,
+                                       krope_dtype == MLA_FP8_E4M3FN, stream),
+                    "gather kernel");
+}
+
+int mla_up_project(void* k_nope_out, void* v_t_out, int32_t k_dtype, const void* latent,
+                   const void* w_k, const void* w_uv, const int32_t* buffer_length_c,
+                   int32_t num_heads, int32_t max_rows, hipStream_t stream) {
+  if (!k_nope_out || !v_t_out || !latent || !w_k || !w_uv || !buffer_length_c)
+    return fail(MLA_ERR_INVALID_ARG, "mla_up_project: null pointer");
+  if (!dtype_ok(k_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_up_project: dtype");
+  if (num_heads < 1 || num_heads > 1024 || max_rows < 64 || max_rows % 64 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "mla_up_project: num_heads=%d max_rows=%d", num_heads,
+                max_rows);
+  mla::GemmArgs g;
+  g.k_out = k_nope_out;
+  g.vt_out = (uint16_t*)v_t_out;
+  g.a = (const uint16_t*)latent;
+  g.wk = (const uint16_t*)w_k;
+  g.wuv = (const uint16_t*)w_uv;
+  g.bl_c = buffer_length_c;
+  g.H = num_heads;
+  g.max_rows = max_rows;
+  return hip_status(mla::launch_up_project(g, k_dtype == MLA_FP8_E4M3FN, stream),
+                    "up-projection kernel");
+}
+
+size_t mla_prefill_attention_workspace_size(int32_t batch_size, int32_t total_q,
+                                            int32_t num_heads) {
+  if (batch_size < 1 || total_q < 0 || num_heads < 1) return 0;
+  return attn_ws_layout(nullptr, batch_size, total_q, num_heads).bytes;
+}
+
+static int attention_common(void* output, const void* q, int32_t dtype, const void* k_nope,
+                            const void* v_t, const void* krope,
+                            const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                            const uint32_t* bro_c, const uint32_t* co_c, const int32_t* bl_c,
+                            int32_t B, int32_t total_q, int32_t H, int32_t max_rows,
+                            float scale, const AttnWs& ws, hipStream_t stream) {
+  mla::AttnArgs a;
+  a.out = (uint16_t*)output;
+  a.q = q;
+  a.k_nope = k_nope;
+  a.v_t = (const uint16_t*)v_t;
+  a.krope = krope;
+  a.offs = input_row_offsets;
+  a.clen = cache_lengths;
+  a.bro_c = bro_c;
+  a.co_c = co_c;
+  a.bl_c = bl_c;
+  a.carry_o = ws.carry_o;
+  a.carry_ml = ws.carry_ml;
+  a.sched = ws.sched;
+  a.n_slots = mla::attn_num_slots(B, total_q);
+  a.B = B;
+  a.H = H;
+  a.max_rows = max_rows;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(mla::launch_prefill_attn(a, dtype == MLA_FP8_E4M3FN, stream),
+                    "attention kernel");
+}
+
+int mla_prefill_attention(void* output, const void* q, int32_t dtype, const void* k_nope,
+                          const void* v_t, const void* krope, const uint32_t* input_row_offsets,
+                          const uint32_t* cache_lengths, const uint32_t* buffer_row_offsets_c,
+                          const uint32_t* cache_offsets_c, const int32_t* buffer_length_c,
+                          int32_t batch_size, int32_t total_q, int32_t num_heads,
+                          int32_t max_rows, int32_t max_prompt_len, float scale,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!output || !q || !k_nope || !v_t || !krope || !input_row_offsets || !cache_lengths ||
+      !buffer_row_offsets_c || !cache_offsets_c || !buffer_length_c)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: null pointer");
+  if (!dtype_ok(dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_attention: dtype");
+  if (batch_size < 1 || total_q < 1 || num_heads < 1 || num_heads > 1024 || max_rows < 64 ||
+      max_rows % 64 != 0 || max_prompt_len < 1 || !(scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: sizes");
+  const size_t need = mla_prefill_attention_workspace_size(batch_size, total_q, num_heads);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "mla_prefill_attention: workspace %zu < %zu",
+                workspace_bytes, need);
+  AttnWs ws = attn_ws_layout((char*)workspace, batch_size, total_q, num_heads);
+  int st = hip_status(mla::launch_attn_schedule(ws.sched, input_row_offsets, batch_size,
+                                                mla::attn_num_slots(batch_size, total_q),
+                                                stream),
+                      "schedule kernel");
+  if (st != MLA_OK) return st;
+  return attention_common(output, q, dtype, k_nope, v_t, krope, input_row_offsets,
+                          cache_lengths, buffer_row_offsets_c, cache_offsets_c,
+                          buffer_length_c, batch_size, total_q, num_heads, max_rows, scale, ws,
+                          stream);
+}
+
+size_t mla_prefill_workspace_size(int32_t batch_size, int32_t total_q, int32_t num_heads,
+                                  int32_t max_rows, int32_t dtype) {
+  if (batch_size < 1 || total_q < 0 || num_heads < 1 || max_rows < 1 || !dtype_ok(dtype))
+    return 0;
+  const int32_t rows = (max_rows + 63) / 64 * 64;
+  return prefill_ws_layout(nullptr, batch_size, total_q, num_heads, rows, dtype).bytes;
+}
+
+int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* input_row_offsets,
+                const uint32_t* cache_lengths, const void* kv_cache, const int32_t* page_table,
+                const uint32_t* buffer_row_offsets, const uint32_t* cache_offsets,
+                const int32_t* buffer_lengths, int32_t max_chunks, int32_t max_rows,
+                const void* w_k, const void* w_uv, const void* kv_norm_gamma,
+                const void* freqs_cis, int32_t batch_size, int32_t total_q, int32_t num_heads,
+                int32_t max_prompt_len, int32_t page_size, int32_t max_pages_per_seq,
+                int32_t num_pages, int32_t max_seq_len, float scale, float epsilon,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!output || !q || !input_row_offsets || !cache_lengths || !kv_cache || !page_table ||
+      !buffer_row_offsets || !cache_offsets || !buffer_lengths || !w_k || !w_uv ||
+      !kv_norm_gamma || !freqs_cis)
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill: null pointer");
+  if (!dtype_ok(dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill: dtype");
+  if (batch_size < 1 || total_q < 1 || num_heads < 1 || num_heads > 1024 || max_chunks < 1 ||
+      max_rows < 1 || max_prompt_len < 1 || page_size < 1 || max_pages_per_seq < 1 ||
+      num_pages < 1 || max_seq_len < 1 || !(scale > 0.f) || !(epsilon >= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill: sizes");
+  const int32_t rows = (max_rows + 63) / 64 * 64;
+  const size_t need =
+      mla_prefill_workspace_size(batch_size, total_q, num_heads, max_rows, dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "mla_prefill: workspace %zu < %zu", workspace_bytes, need);
+  PrefillWs ws =
+      prefill_ws_layout((char*)workspace, batch_size, total_q, num_heads, rows, dtype);
+  const bool fp8 = dtype == MLA_FP8_E4M3FN;
+  int st = hip_status(mla::launch_attn_schedule(ws.attn.sched, input_row_offsets, batch_size,
+                                                mla::attn_num_slots(batch_size, total_q),
+                                                stream),
+                      "schedule kernel");
+  if (st != MLA_OK) return st;
+  for (int c = 0; c < max_chunks; ++c) {
+    const uint32_t* bro_c = buffer_row_offsets + (size_t)c * (batch_size + 1);
+    const uint32_t* co_c = cache_offsets + (size_t)c * batch_size;
+    const int32_t* bl_c = buffer_lengths + c;
+    st = mla_gather_norm_rope(ws.latn, ws.krope, dtype, kv_cache, dtype, page_table, bro_c,
+                              co_c, bl_c, kv_norm_gamma, freqs_cis, batch_size, page_size,
+                              max_pages_per_seq, num_pages, rows, max_seq_len, epsilon, stream);
+    if (st != MLA_OK) return st;
+    st = mla_up_project(ws.k_nope, ws.v_t, dtype, ws.latn, w_k, w_uv, bl_c, num_heads, rows,
+                        stream);
+    if (st != MLA_OK) return st;
+    st = attention_common(output, q, dtype, ws.k_nope, ws.v_t, ws.krope, input_row_offsets,
+                          cache_lengths, bro_c, co_c, bl_c, batch_size, total_q, num_heads,
+                          rows, scale, ws.attn, stream);
+    if (st != MLA_OK) return st;
+  }
+  (void)fp8;
+  return MLA_OK;
+}
+
+size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads, int32_t max_context_len,
+                                 int32_t num_partitions, int32_t cache_dtype) {
+  if (batch_size < 1 || num_heads < 1 || max_context_len < 1 || num_partitions < 0 ||
+      !dtype_ok(cache_dtype))
+    return 0;
+  return decode_ws_layout(nullptr, batch_size, num_heads, max_context_len, num_partitions,
+                          cache_dtype)
+      .bytes;
+}
+
+int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
+               const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+               const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
+               int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+               int32_t max_context_len, int32_t num_partitions, float scale, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (!output || !q || !context_lengths || !kv_cache || !page_table || !w_uk || !w_uv)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer");
+  if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_decode: dtype");
+  if (cache_dtype == MLA_FP8_E4M3FN)
+    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: e4m3 cache not built yet");
+  if (batch_size < 1 || num_heads < 1 || num_heads > 128 || page_size < 1 ||
+      max_pages_per_seq < 1 || num_pages < 1 || max_context_len < 1 || num_partitions < 0 ||
+      !(scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: sizes (num_heads must be 1..128)");
+  const size_t need = mla_decode_workspace_size(batch_size, num_heads, max_context_len,
+                                                num_partitions, cache_dtype);
+  if (!workspace || workspace_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace %zu < %zu", workspace_bytes, need);
+  DecodeWs ws = decode_ws_layout((char*)workspace, batch_size, num_heads, max_context_len,
+                                 num_partitions, cache_dtype);
+  const bool fp8 = cache_dtype == MLA_FP8_E4M3FN;
+  int st = hip_status(mla::launch_decode_absorb(ws.q_abs, (const uint16_t*)q,
+                                                (const uint16_t*)w_uk, batch_size, num_heads,
+                                                fp8, stream),
+                      "absorb kernel");
+  if (st != MLA_OK) return st;
+  mla::DecodeArgs a;
+  a.q_abs = (const uint16_t*)ws.q_abs;
+  a.cache = kv_cache;
+  a.page_table = page_table;
+  a.ctx = context_lengths;
+  a.part_o = ws.part_o;
+  a.part_ml = ws.part_ml;
+  a.B = batch_size;
+  a.H = num_heads;
+  a.ps = page_size;
+  a.maxp = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.P = ws.P;
+  a.keys_per_part = ws.kpp;
+  a.scale_log2 = scale * kLog2e;
+  st = hip_status(mla::launch_decode_split(a, stream), "split-KV kernel");
+  if (st != MLA_OK) return st;
+  st = hip_status(mla::launch_decode_combine(ws.o_lat, ws.part_o, ws.part_ml, context_lengths,
+                                             batch_size, num_heads, ws.P, ws.kpp, stream),
+                  "combine kernel");
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_decode_project((uint16_t*)output, ws.o_lat,
+                                               (const uint16_t*)w_uv, batch_size, num_heads,
+                                               stream),
+                    "projection kernel");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Kernel argument blocks and launchers shared between the libmla HIP sources.
+#pragma once
+
+#include "common.hpp"
+
+namespace mla {
+struct GatherArgs {
+  uint16_t* latn;
+  void* krope;
+  const void* cache;
+  const int32_t* page_table;
+  const uint32_t* bro_c;
+  const uint32_t* co_c;
+  const int32_t* bl_c;
+  const uint16_t* gamma;
+  const uint16_t* freqs;
+  int B, ps, maxp, num_pages, max_rows, max_seq_len;
+  float eps;
+};
+struct GemmArgs {
+  void* k_out;
+  uint16_t* vt_out;
+  const uint16_t* a;
+  const uint16_t* wk;
+  const uint16_t* wuv;
+  const int32_t* bl_c;
+  int H, max_rows;
+};
+struct AttnArgs {
+  uint16_t* out;
+  const void* q;
+  const void* k_nope;
+  const uint16_t* v_t;
+  const void* krope;
+  const uint32_t* offs;
+  const uint32_t* clen;
+  const uint32_t* bro_c;
+  const uint32_t* co_c;
+  const int32_t* bl_c;
+  float* carry_o;
+  float* carry_ml;
+  const int2* sched;
+  int n_slots, B, H, max_rows;
+  float scale_log2;
+};
+struct DecodeArgs {
+  const uint16_t* q_abs;
+  const void* cache;
+  const int32_t* page_table;
+  const uint32_t* ctx;
+  float* part_o;
+  float* part_ml;
+  int B, H, ps, maxp, num_pages, P, keys_per_part;
+  float scale_log2;
+};
+
+hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,
+                       const uint32_t*, int, int, uint32_t, hipStream_t);
+hipError_t launch_gather(const GatherArgs&, bool, bool, hipStream_t);
+hipError_t launch_up_project(const GemmArgs&, bool, hipStream_t);
+int attn_num_slots(int B, int total_q);
+hipError_t launch_attn_schedule(int2*, const uint32_t*, int, int, hipStream_t);
+hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
+hipError_t launch_decode_absorb(void*, const uint16_t*, const uint16_t*, int, int, bool,
+                                hipStream_t);
+hipError_t launch_decode_split(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_combine(uint16_t*, const float*, const float*, const uint32_t*, int,
+                                 int, int, int, hipStream_t);
+hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
+                                 hipStream_t);
+}  // namespace mla

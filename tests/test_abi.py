@@ -1,0 +1,71 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+host arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_chunked_prefill_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libmla.so is not built (run python -m mla_chunked_prefill_amd.build)")
+    return binding.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(-1) == b"invalid argument"
+    assert lib.mla_status_string(-3) == b"workspace missing or too small"
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: validation fails first
+    # null output pointer
+    st = lib.mla_prefill_plan(None, fake, fake, None, fake, fake, 2, 3, 8, None)
+    assert st == -1 and b"null" in lib.mla_last_error()
+    # zero buffer_token_size
+    assert lib.mla_prefill_plan(fake, fake, fake, None, fake, fake, 2, 3, 0, None) == -1
+    # batch * T overflows 31 bits
+    assert lib.mla_prefill_plan(fake, fake, fake, None, fake, fake, 4096, 1, 1 << 20, None) == -1
+    # unsupported dtype
+    assert lib.mla_up_project(fake, fake, 7, fake, fake, fake, fake, 2, 128, None) == -2
+    # max_rows not a multiple of 64
+    assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
+    # workspace too small
+    need = lib.mla_decode_workspace_size(4, 8, 1000, 0, 0)
+    assert need > 0
+    st = lib.mla_decode(fake, fake, fake, fake, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
+                        0.1, fake, need - 1, None)
+    assert st == -3
+    # heads beyond what decode supports
+    assert lib.mla_decode(fake, fake, fake, fake, 0, fake, fake, fake, 4, 256, 16, 100, 50, 1000,
+                          0, 0.1, fake, 1 << 40, None) == -1
+
+
+def test_workspace_sizes_grow_with_problem(lib):
+    a = lib.mla_prefill_workspace_size(2, 100, 4, 256, 0)
+    b = lib.mla_prefill_workspace_size(2, 100, 4, 512, 0)
+    c = lib.mla_prefill_workspace_size(2, 100, 4, 512, 1)
+    assert 0 < a < b and c < b
+    assert lib.mla_prefill_workspace_size(0, 100, 4, 512, 0) == 0
+    assert lib.mla_prefill_attention_workspace_size(2, 100, 4) < a

@@ -1,0 +1,329 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances: the plan is integer work and must be bit-exact. bf16 outputs must be
+within max-abs 2e-2 and mean-abs 2e-3 of the fp64 oracle; outputs computed from
+float8_e4m3fn inputs within max-abs 6e-2. Intermediate products (gather, K/V
+up-projection) are checked per element against a bound derived from their
+rounding: one bf16 rounding of the result (relative 2^-8) plus fp32
+accumulation error.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from workloads import (Dims, decode_recipe, make_decode, make_prefill, prefill_recipe,
+                       prefill_recipe_lengths, f32_to_bf16_bits)
+from workloads.device import bf16_bits, decode_tensors, fp8_bits, prefill_tensors
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, FP8_MAX = 2e-2, 2e-3, 6e-2
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mla_chunked_prefill_amd import binding
+    binding.load()
+    return binding
+
+
+def _f64(t):
+    return oracle.bf16_to_f64(bf16_bits(t))
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _u32(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.uint32)).cuda()
+
+
+# ---------------------------------------------------------------------------
+# plan: bit-exact
+# ---------------------------------------------------------------------------
+
+def _plan_gpu(B, offs, clen, T, C):
+    bro, co, bl, need = B.plan(_u32(offs), _u32(clen), T, C)
+    torch.cuda.synchronize()
+    return (bro.cpu().numpy(), co.cpu().numpy(), bl.cpu().numpy(), int(need.cpu()[0]))
+
+
+@pytest.mark.parametrize("name", ["tiny_b2", "dsv3_prefill_4k", "ragged_b16_cached",
+                                  "fp8_ragged_b8_cached"])
+def test_plan_bit_exact_named(B, name):
+    new, cached, T, C = prefill_recipe_lengths(name)
+    offs = np.concatenate([[0], np.cumsum(new)])
+    _say(f"plan {name}")
+    g = _plan_gpu(B, offs, cached, T, C)
+    r = oracle.plan(offs, cached, T, C)
+    for a, b in zip(g[:3], r):
+        assert a.dtype == b.dtype and np.array_equal(a, b)
+    assert g[3] == -(-int((new + cached).max()) // T)
+
+
+def test_plan_bit_exact_random_and_edges(B):
+    rng = np.random.default_rng(123)
+    cases = []
+    for _ in range(60):
+        Bn = int(rng.integers(1, 40))
+        cases.append((rng.integers(0, 50, Bn), rng.integers(0, 80, Bn), int(rng.integers(1, 20))))
+    cases.append((np.zeros(5, np.int64), np.zeros(5, np.int64), 4))       # nothing at all
+    cases.append((np.array([0, 7, 0]), np.array([3, 0, 0]), 1))             # T = 1
+    cases.append((rng.integers(0, 9, 700), rng.integers(0, 9, 700), 3))     # > 256 sequences
+    cases.append((rng.integers(0, 3000, 1000), rng.integers(0, 3000, 1000), 517))
+    for new, cached, T in cases:
+        offs = np.concatenate([[0], np.cumsum(new)])
+        C = max(1, -(-int((new + cached).max()) // T)) + int(rng.integers(0, 3))
+        g = _plan_gpu(B, offs, cached, T, C)
+        r = oracle.plan(offs, cached, T, C)
+        for a, b in zip(g[:3], r):
+            assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# gather + RMSNorm + RoPE
+# ---------------------------------------------------------------------------
+
+def _gather_case(B, wl, fp8_rope=False):
+    d = oracle.Decoded(wl)
+    t = prefill_tensors(wl)
+    bro, co, bl, _ = B.plan(t["input_row_offsets"], t["cache_lengths"], wl.buffer_token_size,
+                            wl.max_chunks)
+    rbro, rco, rbl = oracle.plan(wl.input_row_offsets, wl.cache_lengths, wl.buffer_token_size,
+                                 wl.max_chunks)
+    R = max(64, (int(wl.batch * wl.buffer_token_size) + 63) // 64 * 64)
+    for c in range(wl.max_chunks):
+        n = int(rbl[c])
+        if n < 0:
+            continue
+        lat = torch.full((R, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+        kr_dtype = torch.float8_e4m3fn if fp8_rope else torch.bfloat16
+        kr = torch.zeros((R, 64), dtype=kr_dtype, device="cuda")
+        B.mla_gather_norm_rope(lat, kr, t["kv_cache"], t["page_table"], bro[c].contiguous(),
+                               co[c].contiguous(), bl[c:c + 1], t["kv_norm_gamma"],
+                               t["freqs_cis"], wl.eps)
+        torch.cuda.synchronize()
+        glat = _f64(lat)[:n]
+        gkr = oracle.e4m3fn_to_f64(fp8_bits(kr))[:n] if fp8_rope else _f64(kr)[:n]
+        for b in range(wl.batch):
+            r0, r1 = int(rbro[c, b]), int(rbro[c, b + 1])
+            if r1 == r0:
+                continue
+            pos = int(rco[c, b]) + np.arange(r1 - r0)
+            raw = oracle.gather_rows(d.pool, wl.page_table, b, pos, wl.page_size)
+            xl, yr = oracle.norm_rope_rows(raw, pos, d.gamma, d.freqs, wl.eps, 512)
+            err = np.abs(glat[r0:r1] - xl)
+            assert (err <= 2.0 ** -8 * np.abs(xl) + 1e-5).all(), err.max()
+            err = np.abs(gkr[r0:r1] - yr)
+            tol = (2.0 ** -3 if fp8_rope else 2.0 ** -8) * np.abs(yr) + (2 ** -9 if fp8_rope else 1e-5)
+            assert (err <= tol).all(), err.max()
+
+
+def test_gather_norm_rope_tiny(B):
+    _gather_case(B, prefill_recipe("tiny_b2"))
+
+
+def test_gather_norm_rope_mid(B):
+    wl = make_prefill("mid", 21, [300, 0, 77, 129], [0, 40, 250, 1000], 2, 16, 256)
+    _gather_case(B, wl)
+
+
+def test_gather_norm_rope_fp8_cache(B):
+    wl = make_prefill("mid8", 22, [100, 33], [70, 0], 2, 16, 64, fp8=True)
+    _gather_case(B, wl, fp8_rope=True)
+
+
+# ---------------------------------------------------------------------------
+# up-projection GEMM
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,R,n", [(2, 128, 128), (3, 256, 201), (1, 64, 1)])
+def test_up_project(B, H, R, n):
+    rng = np.random.default_rng(H * 1000 + n)
+    lat_bits = f32_to_bf16_bits(rng.standard_normal((R, 512), dtype=np.float32))
+    wk_bits = f32_to_bf16_bits(rng.standard_normal((H * 128, 512), dtype=np.float32) / 22.6)
+    wuv_bits = f32_to_bf16_bits(rng.standard_normal((H, 128, 512), dtype=np.float32) / 22.6)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    kn = torch.full((H, R, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vt = torch.full((H, 128, R), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bl = torch.tensor([n], dtype=torch.int32, device="cuda")
+    B.mla_up_project(kn, vt, dev(lat_bits), dev(wk_bits), dev(wuv_bits), bl)
+    torch.cuda.synchronize()
+    lat = oracle.bf16_to_f64(lat_bits)[:n]
+    rk, rv = oracle.up_project(lat, oracle.bf16_to_f64(wk_bits), oracle.bf16_to_f64(wuv_bits), H)
+    gk = _f64(kn)[:, :n].transpose(1, 0, 2)
+    gv = _f64(vt)[:, :, :n].transpose(2, 0, 1)
+    # bound: half an ulp of bf16 on the result plus fp32 accumulation of 512 terms
+    scale_k = np.sqrt((lat ** 2) @ (oracle.bf16_to_f64(wk_bits) ** 2).T).reshape(n, H, 128)
+    assert (np.abs(gk - rk) <= 2.0 ** -8 * np.abs(rk) + 1e-5 * scale_k + 1e-6).all()
+    assert (np.abs(gv - rv) <= 2.0 ** -8 * np.abs(rv) + 1e-5 * np.abs(rv).max() + 1e-5).all()
+
+
+# ---------------------------------------------------------------------------
+# attention on given K/V (one chunk)
+# ---------------------------------------------------------------------------
+
+def test_prefill_attention_given_kv(B):
+    rng = np.random.default_rng(31)
+    H = 3
+    new = np.array([5, 130, 64, 1, 200])
+    cached = np.array([0, 70, 0, 300, 129])
+    L = new + cached
+    offs = np.concatenate([[0], np.cumsum(new)])
+    T = int(L.max())
+    bro, co, bl = oracle.plan(offs, cached, T, 1)
+    R = (int(bl[0]) + 63) // 64 * 64 + 64
+    tq = int(offs[-1])
+    bits = lambda shape, s=1.0: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * s)
+    q_b = bits((tq, H, 192))
+    kn_b = bits((H, R, 128))
+    kr_b = bits((R, 64))
+    vt_b = bits((H, 128, R))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.full((tq, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(B.mla_prefill_attention_workspace_size(len(new), tq, H), dtype=torch.uint8,
+                     device="cuda")
+    scale = 1 / math.sqrt(192)
+    B.mla_prefill_attention(out, dev(q_b), dev(kn_b), dev(vt_b), dev(kr_b), _u32(offs),
+                            _u32(cached), _u32(bro[0]), _u32(co[0]),
+                            torch.tensor(bl, dtype=torch.int32, device="cuda"),
+                            int(new.max()), scale, ws)
+    torch.cuda.synchronize()
+    got = _f64(out)
+    q = oracle.bf16_to_f64(q_b)
+    kn = oracle.bf16_to_f64(kn_b)
+    kr = oracle.bf16_to_f64(kr_b)
+    vt = oracle.bf16_to_f64(vt_b)
+    for b in range(len(new)):
+        r0, r1 = int(bro[0, b]), int(bro[0, b + 1])
+        ref = oracle.attend_sequence(q[offs[b]:offs[b + 1]], kn[:, r0:r1].transpose(1, 0, 2),
+                                     kr[r0:r1], vt[:, :, r0:r1].transpose(2, 0, 1),
+                                     cached[b] + np.arange(new[b]), np.arange(L[b]), scale, 128)
+        err = np.abs(got[offs[b]:offs[b + 1]] - ref)
+        assert err.max() <= BF16_MAX and (err.size == 0 or err.mean() <= BF16_MEAN), (b, err.max())
+
+
+# ---------------------------------------------------------------------------
+# end-to-end prefill
+# ---------------------------------------------------------------------------
+
+def _run_prefill(B, wl, max_rows=None):
+    t = prefill_tensors(wl)
+    out = B.prefill(t["q"], t["input_row_offsets"], t["cache_lengths"], t["kv_cache"],
+                    t["page_table"], t["w_k"], t["w_uv"], t["kv_norm_gamma"], t["freqs_cis"],
+                    wl.buffer_token_size, wl.max_chunks, int(wl.new_lens.max()), wl.scale,
+                    wl.eps, max_rows=max_rows)
+    torch.cuda.synchronize()
+    return _f64(out)
+
+
+def _assert_close(got, ref, max_abs, mean_abs=None):
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    assert err.max() <= max_abs, f"max-abs {err.max():.3e}"
+    if mean_abs is not None:
+        assert err.mean() <= mean_abs, f"mean-abs {err.mean():.3e}"
+    return err
+
+
+def test_prefill_tiny_full(B):
+    wl = prefill_recipe("tiny_b2")
+    _say("prefill tiny_b2")
+    _assert_close(_run_prefill(B, wl), oracle.prefill(wl), BF16_MAX, BF16_MEAN)
+
+
+def test_prefill_multichunk_ragged_full(B):
+    # several 64-key tiles, ragged 128-query blocks, sequences split over chunks,
+    # an empty prompt and pages of 16
+    wl = make_prefill("mid", 41, [300, 77, 0, 129, 1], [0, 250, 33, 1000, 5], 4, 16, 256)
+    _say("prefill mid multichunk")
+    _assert_close(_run_prefill(B, wl), oracle.prefill(wl), BF16_MAX, BF16_MEAN)
+
+
+def test_prefill_single_head_chunk_of_one(B):
+    wl = make_prefill("t1", 42, [9, 3], [4, 0], 1, 16, 1)
+    _assert_close(_run_prefill(B, wl), oracle.prefill(wl), BF16_MAX, BF16_MEAN)
+
+
+def _sample_pairs(wl, n, rng):
+    tq, H = wl.total_q, wl.num_heads
+    offs = wl.input_row_offsets
+    pairs = {(0, 0), (tq - 1, H - 1)}
+    for b in range(wl.batch):
+        if offs[b + 1] > offs[b]:
+            pairs.add((int(offs[b]), int(rng.integers(H))))
+            pairs.add((int(offs[b + 1]) - 1, int(rng.integers(H))))
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(tq)), int(rng.integers(H))))
+    return sorted(pairs)
+
+
+def _sampled_check(B, name, n, max_abs, mean_abs):
+    _say(f"prefill {name}: generating")
+    wl = prefill_recipe(name)
+    _say(f"prefill {name}: running")
+    got = _run_prefill(B, wl)
+    rng = np.random.default_rng(7)
+    pairs = _sample_pairs(wl, n, rng)
+    _say(f"prefill {name}: oracle on {len(pairs)} sampled rows")
+    ref = oracle.prefill_sampled(wl, pairs)
+    g = np.stack([got[t, h] for t, h in pairs])
+    assert np.isfinite(got).all()
+    _assert_close(g, ref, max_abs, mean_abs)
+
+
+def test_prefill_dsv3_4k_sampled(B):
+    _sampled_check(B, "dsv3_prefill_4k", 48, BF16_MAX, BF16_MEAN)
+
+
+def test_prefill_ragged_b16_sampled(B):
+    _sampled_check(B, "ragged_b16_cached", 40, BF16_MAX, BF16_MEAN)
+
+
+def test_prefill_fp8_sampled(B):
+    _sampled_check(B, "fp8_ragged_b8_cached", 40, FP8_MAX, None)
+
+
+def test_prefill_fp8_small_full(B):
+    wl = make_prefill("m8", 43, [70, 5, 140], [0, 60, 9], 2, 16, 128, fp8=True)
+    _assert_close(_run_prefill(B, wl), oracle.prefill(wl), FP8_MAX)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def _run_decode(B, wl, num_partitions=0):
+    t = decode_tensors(wl)
+    out = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
+                   t["w_uv"], int(wl.context_lens.max()), wl.scale,
+                   num_partitions=num_partitions)
+    torch.cuda.synchronize()
+    return _f64(out)
+
+
+@pytest.mark.parametrize("parts", [0, 1, 3])
+def test_decode_small_full(B, parts):
+    wl = make_decode("d", 51, [1, 37, 300, 64, 1000], 8, 16)
+    _assert_close(_run_decode(B, wl, parts), oracle.decode(wl), BF16_MAX, BF16_MEAN)
+
+
+def test_decode_all_heads_full(B):
+    wl = make_decode("d128", 52, [5000, 129, 2], 128, 64)
+    _assert_close(_run_decode(B, wl), oracle.decode(wl), BF16_MAX, BF16_MEAN)
+
+
+def test_decode_b64_sampled(B):
+    _say("decode_b64: generating")
+    wl = decode_recipe("decode_b64")
+    _say("decode_b64: running")
+    got = _run_decode(B, wl)
+    idx = [0, 17, 40, 63]
+    _say("decode_b64: oracle on 4 sequences")
+    ref = oracle.decode(wl, batch_indices=idx)
+    assert np.isfinite(got).all()
+    _assert_close(got[idx], ref, BF16_MAX, BF16_MEAN)

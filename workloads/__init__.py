@@ -7,6 +7,7 @@ from .gen import (  # noqa: F401
     make_prefill,
     make_decode,
     prefill_recipe,
+    prefill_recipe_lengths,
     decode_recipe,
     PREFILL_RECIPES,
     DECODE_RECIPES,

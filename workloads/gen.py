@@ -283,10 +283,7 @@ DECODE_RECIPES = {
 }
 
 
-def prefill_recipe(name: str, **over) -> PrefillWorkload:
-    r = dict(PREFILL_RECIPES[name])
-    r.update(over)
-    rng = np.random.default_rng(r["seed"])
+def _draw_lengths(r: dict, rng: np.random.Generator):
     if isinstance(r["new"], tuple):
         lo, hi = r["new"]
         new = rng.integers(lo, hi + 1, size=r["B"])
@@ -294,6 +291,22 @@ def prefill_recipe(name: str, **over) -> PrefillWorkload:
         cached = rng.integers(clo, chi + 1, size=r["B"])
     else:
         new, cached = r["new"], r["cached"]
+    return np.asarray(new, dtype=np.int64), np.asarray(cached, dtype=np.int64)
+
+
+def prefill_recipe_lengths(name: str):
+    """(new_lens, cached_lens, buffer_token_size, max_chunks) of a named workload,
+    without drawing its tensors."""
+    r = PREFILL_RECIPES[name]
+    new, cached = _draw_lengths(r, np.random.default_rng(r["seed"]))
+    return new, cached, r["T"], r["C"]
+
+
+def prefill_recipe(name: str, **over) -> PrefillWorkload:
+    r = dict(PREFILL_RECIPES[name])
+    r.update(over)
+    rng = np.random.default_rng(r["seed"])
+    new, cached = _draw_lengths(r, rng)
     return make_prefill(name, r["seed"], new, cached, r["H"], r["ps"], r["T"],
                         r.get("C"), fp8=r.get("fp8", False), rng=rng)
 
