@@ -1,0 +1,301 @@
+"""Benchmark: MLA chunked prefill (and absorbed decode) on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+A step is one pass of the prefill path over the DeepSeek-V3-shaped batch (one
+4096-token prompt, no cache, 128 heads): mla_prefill_plan, then for every chunk
+slot mla_gather_norm_rope, mla_up_project and mla_prefill_attention, all
+through the C ABI on torch's current stream. Inputs are resident in HBM before
+the timed region. HIP events recorded on that stream around every call give
+per-call durations; the attention call is the dominant kernel.
+
+A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
+batch (contexts U{4096..32768}) and reports achieved HBM bandwidth.
+
+One JSON line is printed. "value" is the end-to-end prefill rate in
+algorithmic attention TFLOP/s (attention FLOPs / whole step time);
+"roofline" is the attention call alone against the bf16 dense MFMA peak.
+"cpu_baseline" times the fp64 CPU oracle on a bounded sample of the same
+prefill workload (a few of its heads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA prefill attn TFLOP/s & % bf16 MFMA peak; decode HBM GB/s & % peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def visible_pairs(new_lens, cached_lens) -> int:
+    """(query, key) pairs under the cache-shifted causal mask: query i of a
+    sequence with c cached tokens sees c + i + 1 keys."""
+    return int(sum(int(n) * int(c) + int(n) * (int(n) + 1) // 2
+                   for n, c in zip(new_lens, cached_lens)))
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mla_chunked_prefill_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, name: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current source of the kernel; else None."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(kernel_file):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def bench_prefill(args, binding, torch):
+    from workloads import prefill_recipe
+    from workloads.device import prefill_tensors
+
+    wl = prefill_recipe("dsv3_prefill_4k")
+    t = prefill_tensors(wl)
+    B, H, T, C = wl.batch, wl.num_heads, wl.buffer_token_size, wl.max_chunks
+    Tq = wl.total_q
+    lens = wl.seq_lens
+    # host bound on any chunk's rows (the host knows the lengths here)
+    max_rows = int(min(B * T, sum(min(int(L), T) for L in lens)))
+    max_rows = (max_rows + 63) // 64 * 64
+    dev = "cuda"
+    bro = torch.empty((C, B + 1), dtype=torch.uint32, device=dev)
+    co = torch.empty((C, B), dtype=torch.uint32, device=dev)
+    bl = torch.empty((C,), dtype=torch.int32, device=dev)
+    latn = torch.empty((max_rows, 512), dtype=torch.bfloat16, device=dev)
+    krope = torch.empty((max_rows, 64), dtype=torch.bfloat16, device=dev)
+    k_nope = torch.empty((H, max_rows, 128), dtype=torch.bfloat16, device=dev)
+    v_t = torch.empty((H, 128, max_rows), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((Tq, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.mla_prefill_attention_workspace_size(B, Tq, H), dtype=torch.uint8,
+                     device=dev)
+    max_prompt = int(wl.new_lens.max())
+
+    calls = ["plan", "gather", "up_project", "attention"]
+
+    def step(ev):
+        def rec(name, fn):
+            if ev is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                ev.setdefault(name, []).append((e0, e1))
+            else:
+                fn()
+
+        rec("plan", lambda: binding.mla_prefill_plan(bro, co, bl, t["input_row_offsets"],
+                                                     t["cache_lengths"], T))
+        for c in range(C):
+            rec("gather", lambda: binding.mla_gather_norm_rope(
+                latn, krope, t["kv_cache"], t["page_table"], bro[c], co[c], bl[c:c + 1],
+                t["kv_norm_gamma"], t["freqs_cis"], wl.eps))
+            rec("up_project", lambda: binding.mla_up_project(k_nope, v_t, latn, t["w_k"],
+                                                             t["w_uv"], bl[c:c + 1]))
+            rec("attention", lambda: binding.mla_prefill_attention(
+                out, t["q"], k_nope, v_t, krope, t["input_row_offsets"], t["cache_lengths"],
+                bro[c], co[c], bl[c:c + 1], max_prompt, wl.scale, ws))
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ev = {}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    per_call_ms = {}
+    for name in calls:
+        tot = sum(a.elapsed_time(b) for a, b in ev.get(name, []))
+        per_call_ms[name] = tot / args.steps  # ms per step, summed over chunk slots
+    # the attention call of the used chunk: C slots, only chunk 0 has rows here
+    attn_launch_ms = [a.elapsed_time(b) for a, b in ev["attention"]]
+    used = [x for i, x in enumerate(attn_launch_ms) if i % C == 0]
+    attn_ms = sum(used) / len(used)
+    pairs = visible_pairs(wl.new_lens, wl.cached_lens)
+    attn_flop = 2 * (192 + 128) * H * pairs
+    rows = int(sum(lens))
+    gemm_flop = 2 * rows * 512 * 2 * H * 128
+    return dict(
+        wl=wl, wall_ms=wall * 1e3, per_call_ms=per_call_ms, attn_ms=attn_ms,
+        attn_flop=attn_flop, gemm_flop=gemm_flop, pairs=pairs, max_rows=max_rows)
+
+
+def bench_decode(args, binding, torch):
+    from workloads import decode_recipe
+    from workloads.device import decode_tensors
+
+    wl = decode_recipe("decode_b64")
+    t = decode_tensors(wl)
+    B, H = wl.batch, wl.num_heads
+    max_ctx = int(wl.context_lens.max())
+    out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, 0, 0), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        binding.mla_decode(out, t["q"], t["context_lengths"], t["kv_cache"], t["page_table"],
+                           t["w_uk"], t["w_uv"], max_ctx, wl.scale, ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ctx_rows = int(wl.context_lens.astype("int64").sum())
+    bytes_alg = (ctx_rows * 576 * 2 + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2)
+    flop = 2 * (576 + 512) * H * ctx_rows
+    return dict(ms=ms, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows)
+
+
+def cpu_baseline(full_wl, heads: int):
+    """The oracle as it stands on `heads` of the 128 heads of the same prefill
+    workload; returns (attention TFLOP/s on the sample, seconds, threads)."""
+    import dataclasses
+
+    import numpy as np
+
+    from oracle import oracle
+
+    wl = dataclasses.replace(full_wl)
+    d = wl.dims
+    H = wl.num_heads
+    sel = list(range(heads))
+    # restrict the workload to the sampled heads (their q, w_k and w_uv slices)
+    wl.q = wl.q[:, sel]
+    wl.w_k = wl.w_k.reshape(H, d.nope, d.lora)[sel].reshape(-1, d.lora)
+    wl.w_uv = wl.w_uv[sel]
+    wl.w_uk = wl.w_uk[sel]
+    wl.num_heads = heads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    out = oracle.prefill(wl)
+    sec = time.perf_counter() - t0
+    assert np.isfinite(out).all()
+    flop = 2 * (192 + 128) * heads * visible_pairs(wl.new_lens, wl.cached_lens)
+    return flop / sec / 1e12, sec, threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from mla_chunked_prefill_amd import binding
+
+    binding.load()
+    torch.cuda.init()
+    if args.copy_calib:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    p = bench_prefill(args, binding, torch)
+    attn_tflops = p["attn_flop"] / (p["attn_ms"] * 1e-3) / 1e12
+    value = p["attn_flop"] / (p["wall_ms"] * 1e-3) / 1e12
+    traffic = load_traffic("attn.hip", "attn_dsv3_prefill_4k_counters.json")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["wall_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q and latent cache, N(0,1/sqrt(512)) weights)",
+        "config": {"workload": "dsv3_prefill_4k: batch 1, 4096 new tokens, no cache, "
+                               "128 heads, q 192 = 128 nope + 64 rope, v 128, latent 512, "
+                               "page 128, buffer_token_size 8192, causal",
+                   "global_batch": 1, "seq_len": 4096, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_attn_kernel<bf16> (mla_prefill_attention)",
+            "achieved": round(attn_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": p["attn_flop"],
+            "avg_launch_ms": round(p["attn_ms"], 4),
+        },
+        "prefill_breakdown_ms": {k: round(v, 4) for k, v in p["per_call_ms"].items()},
+        "prefill_end_to_end_tflops": round((p["attn_flop"] + p["gemm_flop"]) /
+                                           (p["wall_ms"] * 1e-3) / 1e12, 2),
+    }
+    if not args.no_decode:
+        dd = bench_decode(args, binding, torch)
+        gbps = dd["bytes"] / (dd["ms"] * 1e-3) / 1e9
+        line["decode"] = {
+            "workload": "decode_b64: 64 sequences, one new token each, contexts "
+                        "U{4096..32768}, 128 heads, 576-wide bf16 latent cache, page 64",
+            "ms": round(dd["ms"], 4),
+            "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": dd["bytes"],
+            "tflops": round(dd["flop"] / (dd["ms"] * 1e-3) / 1e12, 2),
+        }
+    if not args.no_cpu:
+        tf, sec, threads = cpu_baseline(p["wl"], args.cpu_heads)
+        line["cpu_baseline"] = {
+            "value": round(tf, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, whole prefill (gather, RMSNorm, RoPE, up-projection, "
+                      f"attention) of dsv3_prefill_4k restricted to {args.cpu_heads} of 128 "
+                      f"heads; {sec:.1f} s; rate in attention FLOPs of the sample",
+            "seconds": round(sec, 2),
+            "host_cpus": len(os.sched_getaffinity(0)),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,9 @@ page, Args). Everything is returned as raw storage bits in numpy arrays:
 uint16 for bf16, uint8 for float8_e4m3fn, so each consumer decodes them itself.
 
 Value recipe (identical for every workload):
-- q, the pool's latent and rope values: N(0, 1) drawn in float32.
+- q, the pool's latent and rope values: N(0, 1) drawn in float32 (tensors of
+  more than 4 * 2^20 values in blocks of 2^20, block k from a generator seeded
+  by one draw of the workload's generator and k).
 - kv_norm_gamma: 1 + N(0, 0.1) (0.1 is the standard deviation).
 - w_k, w_uv, w_uk: N(0, 1/sqrt(512)) (standard deviation 1/sqrt(512)).
 - fp8 workloads: q and the whole pool are each divided by their own absolute
@@ -24,6 +26,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -52,9 +55,13 @@ MLA_DIMS = Dims()
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs stay below 0xFF80_8000 after the rounding add: no overflow
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def f32_to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
@@ -65,9 +72,34 @@ def f32_to_e4m3fn_codes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
+_BLOCK = 1 << 20
+
+
+def _normals(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0, 1) float32 of the given shape. Large tensors are drawn in blocks of
+    2^20 values; block k comes from its own generator seeded by (a draw of the
+    parent generator, k), so the values do not depend on the thread count."""
+    n = int(np.prod(shape))
+    if n <= 4 * _BLOCK:
+        return rng.standard_normal(shape, dtype=np.float32)
+    import concurrent.futures
+    base = int(rng.integers(0, 2 ** 63 - 1))
+    out = np.empty(n, dtype=np.float32)
+
+    def fill(k):
+        g = np.random.default_rng(np.random.SeedSequence(base, spawn_key=(k,)))
+        g.standard_normal(out=out[k * _BLOCK:(k + 1) * _BLOCK], dtype=np.float32)
+
+    nblk = (n + _BLOCK - 1) // _BLOCK
+    workers = min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
+
+
 def _normal_bits(rng: np.random.Generator, shape, std: float = 1.0,
                  mean: float = 0.0) -> np.ndarray:
-    x = rng.standard_normal(shape, dtype=np.float32)
+    x = _normals(rng, shape)
     if std != 1.0:
         x *= np.float32(std)
     if mean != 0.0:
@@ -103,7 +135,7 @@ def _fill_pool(rng: np.random.Generator, lengths: np.ndarray, table: np.ndarray,
                num_pages: int, page_size: int, depth: int, fp8: bool) -> np.ndarray:
     """Pool [num_pages, page_size, depth]; row (b, p) sits at the page table's slot."""
     total = int(np.sum(lengths))
-    vals = rng.standard_normal((total, depth), dtype=np.float32)
+    vals = _normals(rng, (total, depth))
     if fp8:
         amax = float(np.max(np.abs(vals))) if total else 1.0
         vals /= np.float32(amax)
@@ -217,7 +249,7 @@ def make_prefill(name: str, seed: int, new_lens: Sequence[int],
     H = num_heads
     tq = int(offs[-1])
     if fp8:
-        qf = rng.standard_normal((tq, H, dims.q_depth), dtype=np.float32)
+        qf = _normals(rng, (tq, H, dims.q_depth))
         amax = float(np.max(np.abs(qf))) if tq else 1.0
         qf /= np.float32(amax)
         q = f32_to_e4m3fn_codes(qf)
