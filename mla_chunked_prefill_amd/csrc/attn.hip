@@ -39,10 +39,120 @@ constexpr int kVRow = kAttnBN + 8;     // LDS V^T row, bf16 elements (144 B)
 
 typedef long fp8x8;  // 8 e4m3 values in one 64-bit register pair
 
+// Rescale the output accumulator only when a query's running maximum grows by
+// more than this many (log2) units; in between, probabilities are formed
+// against the stale maximum and stay below 2^8, exact in fp32 and bf16 range.
+constexpr float kRescaleSlack = 8.0f;
+
+// Per-thread staging registers of one key tile (global -> registers -> LDS).
+template <bool kFp8>
+struct TileRegs;
+template <>
+struct TileRegs<false> {
+  u32x4 kn[4], kr[2], v[4];
+};
+template <>
+struct TileRegs<true> {
+  u32x4 kn[2], kr[1], v[4];
+};
+
+template <bool kFp8>
+__device__ __forceinline__ void load_tile(TileRegs<kFp8>& R, const AttnArgs& a, int h, int tb,
+                                          int r0, int len, int tid) {
+  const int lo = max(r0, 0);
+  const int hi = min(r0 + len, a.max_rows);
+  const bool full = tb >= lo && tb + kAttnBN <= hi;  // uniform across the workgroup
+  const size_t kbase = (size_t)h * a.max_rows;
+  if (kFp8) {
+    const uint8_t* kn = (const uint8_t*)a.k_nope;
+    const uint8_t* kr = (const uint8_t*)a.krope;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + it * 256;
+      const int gr = tb + (c >> 3);
+      const bool ok = full || (gr >= lo && gr < hi);
+      R.kn[it] = ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + (c & 7) * 16) : u32x4{0, 0, 0, 0};
+    }
+    {
+      const int gr = tb + (tid >> 2);
+      const bool ok = full || (gr >= lo && gr < hi);
+      ((u32x4*)R.kr)[0] = ok ? *(const u32x4*)(kr + (size_t)gr * kRope + (tid & 3) * 16)
+                             : u32x4{0, 0, 0, 0};
+    }
+  } else {
+    const uint16_t* kn = (const uint16_t*)a.k_nope;
+    const uint16_t* kr = (const uint16_t*)a.krope;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid + it * 256;
+      const int gr = tb + (c >> 4);
+      const bool ok = full || (gr >= lo && gr < hi);
+      ((u32x4*)R.kn)[it] =
+          ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + (c & 15) * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + it * 256;
+      const int gr = tb + (c >> 3);
+      const bool ok = full || (gr >= lo && gr < hi);
+      ((u32x4*)R.kr)[it] =
+          ok ? *(const u32x4*)(kr + (size_t)gr * kRope + (c & 7) * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  const uint16_t* vbase = a.v_t + (size_t)h * kV * a.max_rows;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {  // V^T: 128 dims x 8 chunks of 8 keys
+    const int c = tid + it * 256;
+    const int k0 = tb + (c & 7) * 8;
+    u32x4 v = *(const u32x4*)(vbase + (size_t)(c >> 3) * a.max_rows + k0);
+    if (!full && (k0 < lo || k0 + 8 > hi)) {  // zero keys outside this sequence
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ka = k0 + 2 * j;
+        uint32_t w = v[j];
+        if (ka < lo || ka >= hi) w &= 0xFFFF0000u;
+        if (ka + 1 < lo || ka + 1 >= hi) w &= 0x0000FFFFu;
+        v[j] = w;
+      }
+    }
+    R.v[it] = v;
+  }
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void store_tile(const TileRegs<kFp8>& R, uint8_t* sK, uint16_t* sV,
+                                           int tid) {
+  if (kFp8) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + it * 256;
+      *(u32x4*)(sK + (c >> 3) * kKRowFp8 + (c & 7) * 16) = R.kn[it];
+    }
+    *(u32x4*)(sK + (tid >> 2) * kKRowFp8 + kNope + (tid & 3) * 16) = ((const u32x4*)R.kr)[0];
+  } else {
+    uint16_t* k16 = (uint16_t*)sK;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid + it * 256;
+      *(u32x4*)(k16 + (c >> 4) * kKRowBf16 + (c & 15) * 8) = ((const u32x4*)R.kn)[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + it * 256;
+      *(u32x4*)(k16 + (c >> 3) * kKRowBf16 + kNope + (c & 7) * 8) = ((const u32x4*)R.kr)[it];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = tid + it * 256;
+    *(u32x4*)(sV + (c >> 3) * kVRow + (c & 7) * 8) = R.v[it];
+  }
+}
+
 template <bool kFp8>
 __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   constexpr int kKBytes = kFp8 ? kAttnBN * kKRowFp8 : kAttnBN * kKRowBf16 * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t sKraw[kKBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[kKBytes];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kV * kVRow];
 
   // XCD-aware order: consecutive workgroups of one XCD share a head.
@@ -70,8 +180,8 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   if (len <= 0 || q_lo >= n_b) return;
   const int P_hi = c_b + q_hi - 1;
   if (co > P_hi) return;
-  const int kv_end = min(len, P_hi - co + 1);   // keys j < kv_end can be visible
-  const int all_vis = min(len, c_b + q_lo - co + 1);  // keys j < all_vis visible to every query
+  const int kv_end = min(len, P_hi - co + 1);             // keys j < kv_end can be visible
+  const int all_vis = min(len, c_b + q_lo - co + 1);      // keys j < all_vis visible to all
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,7 +215,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   }
 
   f32x16 o[4];
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // reference maximum (log2 domain, scaled)
   float l_run = 0.f;
 #pragma unroll
   for (int md = 0; md < 4; ++md)
@@ -127,77 +237,20 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
 
   // permuted K row fed by this lane: swap bits 2 and 3 of l32
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const float sl2 = a.scale_log2;
 
   const int tile_begin = r0 & ~(kAttnBN - 1);
   // never past the buffer, even if a caller's max_rows is smaller than the chunk
   const int tile_end = min(r0 + kv_end, a.max_rows);
-  const size_t kbase = (size_t)h * a.max_rows;
-  const uint16_t* vbase = a.v_t + (size_t)h * kV * a.max_rows;
+
+  TileRegs<kFp8> R;
+  if (tile_begin < tile_end) load_tile<kFp8>(R, a, h, tile_begin, r0, len, tid);
 
   for (int tb = tile_begin; tb < tile_end; tb += kAttnBN) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile<kFp8>(R, sK, sV, tid);
     __syncthreads();
-    // ---- stage the K tile (nope | rope) and the V^T tile in LDS ----
-    if (kFp8) {
-      const uint8_t* kn = (const uint8_t*)a.k_nope;
-      const uint8_t* kr = (const uint8_t*)a.krope;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {  // nope: 64 rows x 8 chunks
-        const int c = tid + it * 256;
-        const int rr = c >> 3, cc = c & 7;
-        const int gr = tb + rr;
-        const bool ok = gr >= r0 && gr < r0 + len && gr < a.max_rows;
-        u32x4 v = ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + cc * 16) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sKraw + rr * kKRowFp8 + cc * 16) = v;
-      }
-      {  // rope: 64 rows x 4 chunks
-        const int rr = tid >> 2, cc = tid & 3;
-        const int gr = tb + rr;
-        const bool ok = gr >= r0 && gr < r0 + len && gr < a.max_rows;
-        u32x4 v = ok ? *(const u32x4*)(kr + gr * kRope + cc * 16) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sKraw + rr * kKRowFp8 + kNope + cc * 16) = v;
-      }
-    } else {
-      const uint16_t* kn = (const uint16_t*)a.k_nope;
-      const uint16_t* kr = (const uint16_t*)a.krope;
-      uint16_t* sK = (uint16_t*)sKraw;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {  // nope: 64 rows x 16 chunks
-        const int c = tid + it * 256;
-        const int rr = c >> 4, cc = c & 15;
-        const int gr = tb + rr;
-        const bool ok = gr >= r0 && gr < r0 + len && gr < a.max_rows;
-        u32x4 v = ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + cc * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sK + rr * kKRowBf16 + cc * 8) = v;
-      }
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {  // rope: 64 rows x 8 chunks
-        const int c = tid + it * 256;
-        const int rr = c >> 3, cc = c & 7;
-        const int gr = tb + rr;
-        const bool ok = gr >= r0 && gr < r0 + len && gr < a.max_rows;
-        u32x4 v = ok ? *(const u32x4*)(kr + gr * kRope + cc * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sK + rr * kKRowBf16 + kNope + cc * 8) = v;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {  // V^T: 128 dims x 8 chunks of 8 keys
-      const int c = tid + it * 256;
-      const int d = c >> 3, cc = c & 7;
-      const int k0 = tb + cc * 8;
-      u32x4 v = *(const u32x4*)(vbase + (size_t)d * a.max_rows + k0);
-      if (k0 < r0 || k0 + 8 > r0 + len) {  // zero keys outside this sequence
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ka = k0 + 2 * j;
-          uint32_t w = v[j];
-          if (ka < r0 || ka >= r0 + len) w &= 0xFFFF0000u;
-          if (ka + 1 < r0 || ka + 1 >= r0 + len) w &= 0x0000FFFFu;
-          v[j] = w;
-        }
-      }
-      *(u32x4*)(sV + d * kVRow + cc * 8) = v;
-    }
-    __syncthreads();
+    if (tb + kAttnBN < tile_end) load_tile<kFp8>(R, a, h, tb + kAttnBN, r0, len, tid);
     if (!wave_active) continue;
 
     // ---- S^T = K Q^T for 64 keys x 32 queries ----
@@ -211,66 +264,71 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (kFp8) {
-          const fp8x8 ka =
-              *(const fp8x8*)(sKraw + (mb * 32 + kappa) * kKRowFp8 + ks * 16 + hf * 8);
+          const fp8x8 ka = *(const fp8x8*)(sK + (mb * 32 + kappa) * kKRowFp8 + ks * 16 + hf * 8);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ka, qf8[ks], s[mb], 0, 0, 0);
         } else {
-          const bf16x8 ka = *(const bf16x8*)((const uint16_t*)sKraw +
+          const bf16x8 ka = *(const bf16x8*)((const uint16_t*)sK +
                                              (mb * 32 + kappa) * kKRowBf16 + ks * 16 + hf * 8);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[mb], 0, 0, 0);
         }
       }
     }
 
-    // ---- online softmax (log2 domain) ----
+    // ---- online softmax (log2 domain), lazily rescaled ----
     // register i of block mb holds the key at tile row 32*mb + 16*(i/8) + 8*hf + i%8
-    const bool need_mask = (tb < r0) || (tb + kAttnBN > r0 + all_vis);
+    if ((tb < r0) || (tb + kAttnBN > r0 + all_vis)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = tb + mb * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
+          if (kr < r0 || kr > r_hi) s[mb][i] = -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[mb][i] * a.scale_log2;
-        if (need_mask) {
-          const int kr = tb + mb * 32 + (i >> 3) * 16 + hf * 8 + (i & 7);
-          if (kr < r0 || kr > r_hi) v = -INFINITY;
-        }
-        s[mb][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const float mt = tmax * sl2;
+    const bool grow = mt > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int md = 0; md < 4; ++md)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float psum = 0.f;
+    bf16x8 pb[4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[mb][i] - m_use);
-        s[mb][i] = p;
-        psum += p;
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j], sl2, neg_m));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j + 1], sl2, neg_m));
+        psum += p0 + p1;
+        w[j] = pack_bf16x2(p0, p1);
       }
+      pb[ks] = __builtin_bit_cast(bf16x8, w);
+    }
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int md = 0; md < 4; ++md)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      u32x4 pw;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pw[j] = pack_bf16x2(s[ks >> 1][(ks & 1) * 8 + 2 * j], s[ks >> 1][(ks & 1) * 8 + 2 * j + 1]);
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
         const bf16x8 va = *(const bf16x8*)(sV + (md * 32 + l32) * kVRow + ks * 16 + hf * 8);
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[md], 0, 0, 0);
+        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
       }
     }
   }
