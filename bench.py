@@ -150,7 +150,7 @@ def bench_decode(args, binding, torch):
     B, H = wl.batch, wl.num_heads
     max_ctx = int(wl.context_lens.max())
     out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, 0, 0), dtype=torch.uint8,
+    ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, wl.page_size, 0, 0), dtype=torch.uint8,
                      device="cuda")
 
     def call():

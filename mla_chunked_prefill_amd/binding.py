@@ -40,7 +40,7 @@ _SIGNATURES = {
     "mla_prefill_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_prefill": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
                          _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, _S, _P]),
-    "mla_decode_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "mla_decode_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "mla_decode": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                         _P, _S, _P]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -232,9 +232,9 @@ def mla_prefill(output, q, input_row_offsets, cache_lengths, kv_cache, page_tabl
 
 
 def mla_decode_workspace_size(batch_size: int, num_heads: int, max_context_len: int,
-                              num_partitions: int, cache_dtype: int) -> int:
+                              page_size: int, num_partitions: int, cache_dtype: int) -> int:
     return int(load().mla_decode_workspace_size(batch_size, num_heads, max_context_len,
-                                                num_partitions, cache_dtype))
+                                                page_size, num_partitions, cache_dtype))
 
 
 def mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
@@ -306,8 +306,8 @@ def decode(q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len
     if output is None:
         output = torch.empty((B, H, VD), dtype=torch.bfloat16, device=q.device)
     if workspace is None:
-        nbytes = mla_decode_workspace_size(B, H, max_context_len, num_partitions,
-                                           _dtype_code(kv_cache))
+        nbytes = mla_decode_workspace_size(B, H, max_context_len, kv_cache.shape[1],
+                                           num_partitions, _dtype_code(kv_cache))
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
     mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len,
                scale, workspace, num_partitions=num_partitions, stream=stream)

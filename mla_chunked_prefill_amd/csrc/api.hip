@@ -85,42 +85,56 @@ PrefillWs prefill_ws_layout(char* base, int B, int total_q, int H, int max_rows,
   return w;
 }
 
-// decode workspace: q_abs [B][H][576], part_o [B][P][H][512] f32,
-// part_ml [B][P][H][2] f32, o_lat [B][H][512] bf16
-constexpr int kDefaultKeysPerPart = 2048;
-
-int choose_keys_per_part(int B, int max_ctx, int num_partitions) {
-  if (num_partitions > 0) {
-    int kpp = (max_ctx + num_partitions - 1) / num_partitions;
-    kpp = (kpp + 31) / 32 * 32;  // whole key tiles
-    return kpp < 32 ? 32 : kpp;
+// decode workspace: q_abs [B][H][576], cum [B+1] u32, part_o [G+B][H][512] f32,
+// part_ml [G+B][H][2] f32, o_lat [B][H][2][512] bf16 (hi, lo). G split workgroups cover
+// the batch's concatenated contexts in equal ranges.
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    return 256;  // MI355X
   }
-  (void)B;
-  return kDefaultKeysPerPart;
+  return n;
+}
+
+// Split workgroups over the batch. Each one's key range must span at most
+// 2046 pages (the page-table window it stages in LDS).
+int decode_groups(int B, int max_ctx, int page_size, int num_partitions) {
+  int g = num_partitions > 0 ? num_partitions : device_cu_count();
+  const long long keys = (long long)B * max_ctx;
+  const long long per_group = 2046LL * page_size - 1;
+  const long long need = (keys + per_group - 1) / per_group;
+  if (g < need) g = (int)need;
+  return g;
 }
 
 struct DecodeWs {
   void* q_abs;
+  uint32_t* cum;
   float* part_o;
   float* part_ml;
   uint16_t* o_lat;
-  int P, kpp;
+  int G;
   size_t bytes;
 };
-DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int num_partitions,
-                          int cache_dtype) {
+DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
+                          int num_partitions, int cache_dtype) {
   DecodeWs w;
-  w.kpp = choose_keys_per_part(B, max_ctx, num_partitions);
-  w.P = (max_ctx + w.kpp - 1) / w.kpp;
+  w.G = decode_groups(B, max_ctx, page_size, num_partitions);
+  const size_t slots = (size_t)w.G + B;
   size_t off = 0;
   w.q_abs = base + off;
   off = align_up(off + (size_t)B * H * mla::kCache * dsize(cache_dtype));
+  w.cum = (uint32_t*)(base + off);
+  off = align_up(off + (size_t)(B + 1) * sizeof(uint32_t));
   w.part_o = (float*)(base + off);
-  off = align_up(off + (size_t)B * w.P * H * mla::kLora * sizeof(float));
+  off = align_up(off + slots * H * mla::kLora * sizeof(float));
   w.part_ml = (float*)(base + off);
-  off = align_up(off + (size_t)B * w.P * H * 2 * sizeof(float));
+  off = align_up(off + slots * H * 2 * sizeof(float));
   w.o_lat = (uint16_t*)(base + off);
-  off = align_up(off + (size_t)B * H * mla::kLora * 2);
+  off = align_up(off + (size_t)B * H * 2 * mla::kLora * 2);  // hi and lo
   w.bytes = off;
   return w;
 }
@@ -345,12 +359,12 @@ int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* inpu
 }
 
 size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads, int32_t max_context_len,
-                                 int32_t num_partitions, int32_t cache_dtype) {
-  if (batch_size < 1 || num_heads < 1 || max_context_len < 1 || num_partitions < 0 ||
-      !dtype_ok(cache_dtype))
+                                 int32_t page_size, int32_t num_partitions, int32_t cache_dtype) {
+  if (batch_size < 1 || num_heads < 1 || max_context_len < 1 || page_size < 1 ||
+      num_partitions < 0 || !dtype_ok(cache_dtype))
     return 0;
-  return decode_ws_layout(nullptr, batch_size, num_heads, max_context_len, num_partitions,
-                          cache_dtype)
+  return decode_ws_layout(nullptr, batch_size, num_heads, max_context_len, page_size,
+                          num_partitions, cache_dtype)
       .bytes;
 }
 
@@ -367,25 +381,32 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
     return fail(MLA_ERR_UNSUPPORTED, "mla_decode: e4m3 cache not built yet");
   if (batch_size < 1 || num_heads < 1 || num_heads > 128 || page_size < 1 ||
       max_pages_per_seq < 1 || num_pages < 1 || max_context_len < 1 || num_partitions < 0 ||
-      !(scale > 0.f))
+      num_partitions > 65536 || !(scale > 0.f))
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: sizes (num_heads must be 1..128)");
+  if ((uint64_t)batch_size * (uint64_t)max_context_len >= (1ull << 31) ||
+      (uint64_t)num_pages * (uint64_t)page_size >= (1ull << 31))
+    return fail(MLA_ERR_INVALID_ARG,
+                "mla_decode: batch_size * max_context_len and num_pages * page_size must be < 2^31");
   const size_t need = mla_decode_workspace_size(batch_size, num_heads, max_context_len,
-                                                num_partitions, cache_dtype);
+                                                page_size, num_partitions, cache_dtype);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace %zu < %zu", workspace_bytes, need);
   DecodeWs ws = decode_ws_layout((char*)workspace, batch_size, num_heads, max_context_len,
-                                 num_partitions, cache_dtype);
+                                 page_size, num_partitions, cache_dtype);
   const bool fp8 = cache_dtype == MLA_FP8_E4M3FN;
   int st = hip_status(mla::launch_decode_absorb(ws.q_abs, (const uint16_t*)q,
                                                 (const uint16_t*)w_uk, batch_size, num_heads,
                                                 fp8, stream),
                       "absorb kernel");
   if (st != MLA_OK) return st;
+  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, stream),
+                  "prefix kernel");
+  if (st != MLA_OK) return st;
   mla::DecodeArgs a;
   a.q_abs = (const uint16_t*)ws.q_abs;
   a.cache = kv_cache;
   a.page_table = page_table;
-  a.ctx = context_lengths;
+  a.cum = ws.cum;
   a.part_o = ws.part_o;
   a.part_ml = ws.part_ml;
   a.B = batch_size;
@@ -393,14 +414,27 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   a.ps = page_size;
   a.maxp = max_pages_per_seq;
   a.num_pages = num_pages;
-  a.P = ws.P;
-  a.keys_per_part = ws.kpp;
+  a.G = ws.G;
+  a.halves = num_heads > 64 ? 2 : 1;
   a.scale_log2 = scale * kLog2e;
   st = hip_status(mla::launch_decode_split(a, stream), "split-KV kernel");
   if (st != MLA_OK) return st;
-  st = hip_status(mla::launch_decode_combine(ws.o_lat, ws.part_o, ws.part_ml, context_lengths,
-                                             batch_size, num_heads, ws.P, ws.kpp, stream),
-                  "combine kernel");
+  mla::CombineArgs c;
+  c.o_lat = ws.o_lat;
+  c.part_o = ws.part_o;
+  c.part_ml = ws.part_ml;
+  c.cum = ws.cum;
+  c.q_abs = (const uint16_t*)ws.q_abs;
+  c.cache = kv_cache;
+  c.page_table = page_table;
+  c.B = batch_size;
+  c.H = num_heads;
+  c.G = ws.G;
+  c.ps = page_size;
+  c.maxp = max_pages_per_seq;
+  c.num_pages = num_pages;
+  c.scale_log2 = scale * kLog2e;
+  st = hip_status(mla::launch_decode_combine(c, stream), "combine kernel");
   if (st != MLA_OK) return st;
   return hip_status(mla::launch_decode_project((uint16_t*)output, ws.o_lat,
                                                (const uint16_t*)w_uv, batch_size, num_heads,

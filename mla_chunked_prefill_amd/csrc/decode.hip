@@ -31,7 +31,7 @@ typedef long fp8x8_d;
 // X rows: x + b*x_stride (K contiguous, bf16); W rows: w + n*K (K contiguous).
 // Output: y[b*y_stride + n] as bf16 (or e4m3 when kFp8Out). One wave computes a
 // 32 (b) x 32 (n) tile; K is a multiple of 16.
-template <int K, bool kFp8Out>
+template <int K, bool kFp8Out, bool kTwoTerm = false>
 __global__ void __launch_bounds__(256) head_gemm_kernel(
     void* __restrict__ y, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     int B, int N, long x_stride_b, long x_stride_h, long w_stride_h, long y_stride_b,
@@ -60,6 +60,12 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
     const u32x4 wb = *(const u32x4*)(wp + k0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
                                                   __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+    if (kTwoTerm) {  // x = hi + lo, lo stored K elements after hi
+      u32x4 xl = *(const u32x4*)(xp + K + k0);
+      if (brow >= B) xl = u32x4{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xl),
+                                                    __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
+    }
   }
   // lane holds column n = nrow, rows b = tb*32 + 8*(i/4) + 4*hf + i%4
 #pragma unroll
@@ -87,203 +93,430 @@ __global__ void copy_rope_kernel(void* __restrict__ q_abs, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// 2. split-KV attention over the latent cache (bf16 cache)
+// 2. balanced split-KV attention over the latent cache (bf16 cache)
 // ---------------------------------------------------------------------------
-constexpr int kDecBN = 32;                 // keys per tile
-constexpr int kZRow = kCache + 8;          // LDS row of Z (bf16 elements, 1168 B)
-constexpr int kZtRow = kDecBN + 8;         // LDS row of Z^T (bf16 elements, 80 B)
+// The batch's contexts are laid end to end (N keys in all) and key range w of G
+// covers keys [w*N/G, (w+1)*N/G): every range streams the same number of rows
+// whatever the mix of context lengths. A range writes one partial state per
+// sequence it touches, into slot w + b (injective over the touching pairs, at
+// most G + B slots).
+//
+// Two workgroups share a range, one per half of the heads (64 each); they are
+// numbered so that both land on the same XCD back to back and the second read
+// of every tile hits that XCD's L2. A workgroup has four waves, one per SIMD:
+// head group hg = wave & 1 (32 heads) and half dh = wave >> 1. For the scores
+// S^T = Z Q^T (keys x heads, mfma 32x32x16: per-lane softmax statistics) a wave
+// reduces its 288 of the 576 depths and the two waves of a head group add their
+// partial score tiles through LDS; for the values O^T += Z^T P^T a wave keeps
+// its 256 of the 512 latent dims, reading Z^T straight from the row-major tile
+// with transposed LDS reads.
+//
+// The accumulator is never rescaled: each lane takes its first tile's maximum
+// as the reference and later probabilities are formed against it (exact in
+// bf16 and fp32 while below 2^64). A wave whose scores would exceed that
+// marks its partials invalid (with the exact maximum of the segment, which it
+// keeps tracking) and the combine step recomputes them.
+//
+// Tiles of 32 rows are triple-buffered in LDS by direct global->LDS loads; a
+// row occupies 73 16-byte chunks (72 + one pad chunk) so that reads of one
+// column across rows, and the transposed reads, hit distinct banks.
+constexpr int kDecWaves = 4;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecHeads = 64;                     // heads per workgroup
+constexpr int kDecBN = 32;                        // rows per tile
+constexpr int kZRowChunks = 73;                   // 16-byte chunks per LDS row
+constexpr int kZRowB = kZRowChunks * 16;          // 1168 bytes
+constexpr int kZLoads = (kDecBN * kZRowChunks + 63) / 64;  // 37 wave loads of 1 KB
+constexpr int kZStageB = kZLoads * 1024;          // 37888 bytes
+constexpr int kZStages = 3;
+constexpr int kDmaPerWave = (kZLoads + kDecWaves - 1) / kDecWaves;  // 10
+constexpr int kPTWindow = 2048;                   // page-table entries staged per segment
 
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ uint32_t sel_lo16(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
+// transposed 4 x 16-bit read: lane i of each 16-lane group receives element
+// i % 4 of the 8 bytes addressed by lane 4k + i / 4, for k = 0..3
+__device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* lds_byte_ptr) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte_ptr)));
 }
-__device__ __forceinline__ uint32_t sel_hi16(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_dst + 16 l (lds_dst is wave-uniform). Issued as inline assembly so that
+// the compiler does not treat later LDS reads of other stages as dependent on
+// it (it would wait for every load in flight); the kernel orders these loads
+// itself with s_waitcnt vmcnt, counting in issue order, and barriers.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_dst) {
+  const uint32_t lds_addr = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "memory", "m0");
 }
 
-__global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sZ[kDecBN * kZRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sZt[kLora * kZtRow];
+__global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
+  __shared__ __attribute__((aligned(16))) float sX[kDecWaves * 16 * 64];
+  __shared__ int sPT[kPTWindow];
 
-  const int b = blockIdx.x / a.P;
-  const int part = blockIdx.x - b * a.P;
-  const int ctx = (int)a.ctx[b];
-  const int k_begin = part * a.keys_per_part;
-  if (k_begin >= ctx) return;
-  const int k_end = min(ctx, k_begin + a.keys_per_part);
+  // workgroup -> (key range, head half); the two halves of a range share an XCD
+  const int L = blockIdx.x;
+  const int w = a.halves == 2 ? (L >> 4) * 8 + (L & 7) : L;
+  const int half = a.halves == 2 ? (L >> 3) & 1 : 0;
+  if (w >= a.G) return;
+  const uint32_t N = a.cum[a.B];
+  const uint32_t s_lo = (uint32_t)(((uint64_t)w * N) / a.G);
+  const uint32_t s_hi = (uint32_t)(((uint64_t)(w + 1) * N) / a.G);
+  if (s_lo >= s_hi) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave & 1;
+  const int dh = wave >> 1;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int head = wave * 32 + l32;  // this lane's query column
+  const int head = half * kDecHeads + hg * 32 + l32;
   const bool hvalid = head < a.H;
-
-  bf16x8 qf[36];
-  {
-    const uint16_t* qp = a.q_abs + ((long)b * a.H + min(head, a.H - 1)) * kCache + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      u32x4 v = hvalid ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  f32x16 o[16];
-#pragma unroll
-  for (int md = 0; md < 16; ++md)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const float sl2 = a.scale_log2;
   const uint16_t* cache = (const uint16_t*)a.cache;
 
-  // loader roles: latent: dim chunk dc (0..63) x key group kg (0..3) of 8 keys
-  const int dc = tid & 63;
-  const int kg = tid >> 6;
-  for (int kt = k_begin; kt < k_end; kt += kDecBN) {
-    __syncthreads();
-    {
-      u32x4 r[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int p = kt + kg * 8 + j;
-        bool ok = p < k_end;
-        long slot = 0;
-        if (ok) {
-          const int lp = p / a.ps;
-          const int pg = lp < a.maxp ? a.page_table[(long)b * a.maxp + lp] : -1;
-          ok = pg >= 0 && pg < a.num_pages;
-          slot = (long)pg * a.ps + (p - lp * a.ps);
-        }
-        r[j] = ok ? *(const u32x4*)(cache + slot * kCache + dc * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sZ + (kg * 8 + j) * kZRow + dc * 8) = r[j];
-      }
-      // 8x8 transpose: Z^T[8*dc + d][8*kg + j]
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        u32x4 t;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t a0 = r[2 * i][d >> 1];
-          const uint32_t a1 = r[2 * i + 1][d >> 1];
-          t[i] = (d & 1) ? sel_hi16(a0, a1) : sel_lo16(a0, a1);
-        }
-        *(u32x4*)(sZt + (dc * 8 + d) * kZtRow + kg * 8) = t;
-      }
-      // rope columns: 32 keys x 8 chunks
-      {
-        const int kk = tid >> 3, ch = tid & 7;
-        const int p = kt + kk;
-        bool ok = p < k_end;
-        long slot = 0;
-        if (ok) {
-          const int lp = p / a.ps;
-          const int pg = lp < a.maxp ? a.page_table[(long)b * a.maxp + lp] : -1;
-          ok = pg >= 0 && pg < a.num_pages;
-          slot = (long)pg * a.ps + (p - lp * a.ps);
-        }
-        const u32x4 v = ok ? *(const u32x4*)(cache + slot * kCache + kLora + ch * 8)
-                           : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sZ + kk * kZRow + kLora + ch * 8) = v;
-      }
+  // per-lane LDS byte offsets (within a stage)
+  const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  const int s_off = kappa * kZRowB + (36 * dh + hf) * 16;  // + 32 * ks
+  const int g16 = lane >> 4, L16 = lane & 15;
+  // transposed reads: row 16*ks + 8*(g16/2) + 4*t + L16/4, dims 256*dh + 32*md +
+  // 16*(g16&1) + 4*(L16&3)
+  const int tr_base = (8 * (g16 >> 1) + (L16 >> 2)) * kZRowB +
+                      (32 * dh + 2 * (g16 & 1) + ((L16 >> 1) & 1)) * 16 + (L16 & 1) * 8;
+  const int my_loads = (wave + kDecWaves * (kDmaPerWave - 1) < kZLoads) ? kDmaPerWave
+                                                                         : kDmaPerWave - 1;
+
+  // first sequence touched: largest b with cum[b] <= s_lo
+  int b;
+  {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cum[mid] <= s_lo) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  uint32_t pos = s_lo;
+  while (pos < s_hi) {
+    const uint32_t seg_end = min(s_hi, a.cum[b + 1]);
+    if (seg_end <= pos) { ++b; continue; }
+    const int k0 = (int)(pos - a.cum[b]);
+    const int k1 = (int)(seg_end - a.cum[b]);
+    const int ntiles = (k1 - k0 + kDecBN - 1) / kDecBN;
+    // the segment's page-table entries, staged in LDS once: the DMA queue then
+    // holds only tile loads, so waits on it never stall for a table lookup
+    const int lp0 = k0 / a.ps;
+    const int npg = (k1 - 1) / a.ps - lp0 + 1;
+    __syncthreads();  // the previous segment is done with the page window and the stages
+    for (int i = tid; i < min(npg, kPTWindow); i += kDecThreads) {
+      const int lp = lp0 + i;
+      int pg = lp < a.maxp ? a.page_table[(size_t)b * a.maxp + lp] : 0;
+      sPT[i] = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
     }
     __syncthreads();
 
-    f32x16 s;
+    auto issue = [&](int tile, int stage) {
+      uint8_t* base = sZ + stage * kZStageB;
+      const int kt = k0 + tile * kDecBN;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+      for (int i = 0; i < kDmaPerWave; ++i) {
+        const int j = wave + kDecWaves * i;
+        if (j < kZLoads) {
+          // LDS chunk position p = 64 j + lane holds (row, col) of the tile; the
+          // pad chunk of a row and the tail of the last load fetch valid data
+          const int p = j * 64 + lane;
+          int row = p / kZRowChunks;
+          int col = p - row * kZRowChunks;
+          if (col == kZRowChunks - 1) col = 0;
+          if (row >= kDecBN) { row = kDecBN - 1; col = 0; }
+          const int key = min(kt + row, k1 - 1);  // rows past the segment: a valid row
+          const int lp = key / a.ps;
+          const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+          dma16(cache + ((size_t)slot * kCache + col * 8), base + j * 1024);
+        }
+      }
+    };
+
+    // absorbed queries of this wave's heads and depth half: 18 steps of 16
+    bf16x8 qf[18];
+    {
+      const uint16_t* qp =
+          a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache + 288 * dh + hf * 8;
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) {
-      const bf16x8 za = *(const bf16x8*)(sZ + kappa * kZRow + ks * 16 + hf * 8);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qf[ks], s, 0, 0, 0);
-    }
-    // register i holds key kt + 16*(i/8) + 8*hf + i%8
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v = s[i] * a.scale_log2;
-      const int kk = kt + (i >> 3) * 16 + hf * 8 + (i & 7);
-      if (kk >= k_end) v = -INFINITY;
-      s[i] = v;
-      tmax = fmaxf(tmax, v);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(s[i] - m_new);
-      s[i] = p;
-      psum += p;
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(s[ks * 8 + 2 * j], s[ks * 8 + 2 * j + 1]);
-      pb[ks] = __builtin_bit_cast(bf16x8, w);
-    }
-#pragma unroll
-    for (int md = 0; md < 16; ++md) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[md][i] *= alpha;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 za = *(const bf16x8*)(sZt + (md * 32 + l32) * kZtRow + ks * 16 + hf * 8);
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, pb[ks], o[md], 0, 0, 0);
+      for (int ks = 0; ks < 18; ++ks) {
+        u32x4 v = hvalid ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-  }
-  if (!hvalid) return;
-  // O^T register i of block md: dim 32*md + 8*(i/4) + 4*hf + i%4
-  const long base = (((long)b * a.P + part) * a.H + head);
-  float* op = a.part_o + base * kLora;
+    // wait for q here, before any tile load is in flight: the compiler cannot
+    // count the tile loads, so a wait it placed for q inside the tile loop
+    // would drain them every tile (gfx9 encoding: vmcnt 0, others unlimited)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    float m_ref = -INFINITY;   // reference maximum (log2 domain)
+    float m_seen = -INFINITY;  // largest scaled score of the segment (exact at the end)
+    f32x16 o[8];
 #pragma unroll
-  for (int md = 0; md < 16; ++md)
+    for (int md = 0; md < 8; ++md)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 v;
+      for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
+    float l_run = 0.f;
+    bool halted = false;  // wave-uniform: the partial is marked for recomputation
+
+    issue(0, 0);
+    if (ntiles > 1) issue(1, 1);
+
+    for (int t = 0; t < ntiles; ++t) {
+      // wait for this wave's loads of tile t (tile t+1's may stay in flight)
+      if (t + 1 < ntiles) {
+        if (my_loads == kDmaPerWave) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      if (t + 2 < ntiles) issue(t + 2, (t + 2) % kZStages);
+      const uint8_t* Z = sZ + (t % kZStages) * kZStageB;
+      const int kt = k0 + t * kDecBN;
+
+      // partial scores over this wave's depth half
+      f32x16 s;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
-      *(f32x4*)(op + md * 32 + g * 8 + hf * 4) = v;
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const bf16x8 za = *(const bf16x8*)(Z + s_off + 32 * ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qf[ks], s, 0, 0, 0);
+      }
+      float* xw = sX + wave * 1024;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xw[i * 64 + lane] = s[i];
+      __syncthreads();
+      const float* xp = sX + (wave ^ 2) * 1024;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] += xp[i * 64 + lane];
+
+      // register i holds tile row 16*(i/8) + 8*hf + i%8
+      if (kt + kDecBN > k1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kt + (i >> 3) * 16 + hf * 8 + (i & 7) >= k1) s[i] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mt = tmax * sl2;  // finite: every tile holds a valid row
+      m_seen = fmaxf(m_seen, mt);
+      if (m_ref == -INFINITY) m_ref = mt;
+      halted = halted || (__ballot(mt > m_ref + 64.0f) != 0);
+      const float neg_m = -m_ref;
+      float psum = 0.f;
+      bf16x8 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 wv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j], sl2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j + 1], sl2, neg_m));
+          psum += p0 + p1;
+          wv[j] = pack_bf16x2(p0, p1);
+        }
+        pb[ks] = __builtin_bit_cast(bf16x8, wv);
+      }
+      psum += __shfl_xor(psum, 32, 64);
+      l_run += psum;
+
+      // O^T[256 dims x 32 heads] += Z^T P^T, Z^T read transposed from the row tile
+#pragma unroll
+      for (int md = 0; md < 8; ++md)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x4 a0 = ds_read_tr16(Z + tr_base + 16 * ks * kZRowB + 64 * md);
+          const bf16x4 a1 = ds_read_tr16(Z + tr_base + (16 * ks + 4) * kZRowB + 64 * md);
+          const bf16x8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
+        }
     }
-  if (hf == 0) {
-    a.part_ml[base * 2 + 0] = m_run;
-    a.part_ml[base * 2 + 1] = l_run;
+
+    // partial state of (w, b): slot w + b
+    if (hvalid) {
+      const size_t base = ((size_t)(w + b) * a.H + head);
+      float* op = a.part_o + base * kLora + 256 * dh;
+      // O^T register i of block md: dim 32*md + 8*(i/4) + 4*hf + i%4 (within the half)
+#pragma unroll
+      for (int md = 0; md < 8; ++md)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
+          *(f32x4*)(op + md * 32 + g * 8 + hf * 4) = v;
+        }
+      if (hf == 0 && dh == 0) {
+        // an overflowing head group hands (exact maximum, -1) to the combine
+        // step, which recomputes this partial against that maximum
+        // (both waves of a head group hold the same summed scores and flags)
+        a.part_ml[base * 2 + 0] = halted ? m_seen : m_ref;
+        a.part_ml[base * 2 + 1] = halted ? -1.0f : l_run;
+      }
+    }
+    pos = seg_end;
+    ++b;
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine partitions: o_lat[b, h, :] (bf16)
+// prefix sums of the context lengths (one workgroup)
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) decode_combine_kernel(
-    uint16_t* __restrict__ o_lat, const float* __restrict__ part_o,
-    const float* __restrict__ part_ml, const uint32_t* __restrict__ ctx, int H, int P,
-    int keys_per_part) {
+__global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const uint32_t* ctx,
+                                                            int B) {
+  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    const uint32_t v = b < B ? ctx[b] : 0u;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const uint32_t x = tid >= d ? s_scan[tid - d] : 0u;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    if (b < B) cum[b + 1] = s_carry + s_scan[tid];
+    __syncthreads();
+    if (tid == 255) s_carry += s_scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) cum[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// 3. combine partial states: o_lat[b, h, :] (bf16)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t split_start(int w, uint32_t N, int G) {
+  return (uint32_t)(((uint64_t)w * N) / G);
+}
+
+// Recompute the partial of (range w, sequence b, head h) against the exact
+// maximum m (log2 domain) the split kernel recorded. Plain fp32 arithmetic,
+// one key per thread for the scores; only reached for extreme score ranges.
+__device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, float m,
+                                  float* sh_q, float* sh_p) {
+  const int tid = threadIdx.x;
+  const uint32_t N = c.cum[c.B];
+  const uint32_t lo = max(split_start(w, N, c.G), c.cum[b]);
+  const uint32_t hi = min(split_start(w + 1, N, c.G), c.cum[b + 1]);
+  const int k0 = (int)(lo - c.cum[b]), k1 = (int)(hi - c.cum[b]);
+  const uint16_t* qa = c.q_abs + ((size_t)b * c.H + h) * kCache;
+  for (int e = tid; e < kCache; e += 256) sh_q[e] = bf16_to_f32(qa[e]);
+  __syncthreads();
+  const uint16_t* cache = (const uint16_t*)c.cache;
+  auto row_of = [&](int key) -> const uint16_t* {
+    const int lp = key / c.ps;
+    int pg = lp < c.maxp ? c.page_table[(size_t)b * c.maxp + lp] : 0;
+    if (pg < 0 || pg >= c.num_pages) pg = 0;
+    return cache + ((size_t)pg * c.ps + (key - lp * c.ps)) * kCache;
+  };
+  float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+  const int d = 2 * tid;
+  for (int kc = k0; kc < k1; kc += 256) {
+    const int key = kc + tid;
+    float p = 0.f;
+    if (key < k1) {
+      const uint16_t* z = row_of(key);
+      float sc = 0.f;
+      for (int e = 0; e < kCache; ++e) sc = fmaf(sh_q[e], bf16_to_f32(z[e]), sc);
+      p = __builtin_amdgcn_exp2f(sc * c.scale_log2 - m);
+    }
+    sh_p[tid] = p;
+    __syncthreads();
+    const int n = min(256, k1 - kc);
+    for (int k = 0; k < n; ++k) {
+      const float pk = sh_p[k];
+      const uint16_t* z = row_of(kc + k);
+      acc0 = fmaf(pk, bf16_to_f32(z[d]), acc0);
+      acc1 = fmaf(pk, bf16_to_f32(z[d + 1]), acc1);
+      lsum += pk;
+    }
+    __syncthreads();
+  }
+  const size_t base = (size_t)(w + b) * c.H + h;
+  c.part_o[base * kLora + d] = acc0;
+  c.part_o[base * kLora + d + 1] = acc1;
+  __syncthreads();
+  if (tid == 0) {
+    c.part_ml[base * 2 + 0] = m;
+    c.part_ml[base * 2 + 1] = lsum;
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
+  __shared__ float sh_q[kCache];
+  __shared__ float sh_p[256];
   // one workgroup per (b, h); 256 threads x 2 dims
   const int bh = blockIdx.x;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const int np = min(P, (int)((ctx[b] + keys_per_part - 1) / keys_per_part));
+  const int b = bh / c.H;
+  const int h = bh - b * c.H;
+  const uint32_t N = c.cum[c.B];
+  const uint32_t lo_key = c.cum[b], hi_key = c.cum[b + 1];  // keys [lo_key, hi_key)
+  if (hi_key <= lo_key) return;
+  // ranges touching the sequence: w_lo holds lo_key, w_hi holds hi_key - 1
+  int w_lo, w_hi;
+  {
+    int lo = 0, hi = c.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (split_start(mid, N, c.G) <= lo_key) lo = mid; else hi = mid - 1;
+    }
+    w_lo = lo;
+    lo = w_lo; hi = c.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (split_start(mid, N, c.G) < hi_key) lo = mid; else hi = mid - 1;
+    }
+    w_hi = lo;
+  }
   float M = -INFINITY;
-  for (int s = 0; s < np; ++s) M = fmaxf(M, part_ml[(((long)b * P + s) * H + h) * 2]);
+  for (int w = w_lo; w <= w_hi; ++w) {
+    if (split_start(w, N, c.G) >= split_start(w + 1, N, c.G)) continue;  // empty range
+    const size_t base = (size_t)(w + b) * c.H + h;
+    const float m = c.part_ml[base * 2];
+    if (c.part_ml[base * 2 + 1] < 0.f) recompute_partial(c, w, b, h, m, sh_q, sh_p);
+    M = fmaxf(M, m);
+  }
   float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
   const int d = threadIdx.x * 2;
-  for (int s = 0; s < np; ++s) {
-    const long base = ((long)b * P + s) * H + h;
-    const float w = __builtin_amdgcn_exp2f(part_ml[base * 2] - M);
-    lsum += w * part_ml[base * 2 + 1];
-    acc0 += w * part_o[base * kLora + d];
-    acc1 += w * part_o[base * kLora + d + 1];
+  for (int w = w_lo; w <= w_hi; ++w) {
+    if (split_start(w, N, c.G) >= split_start(w + 1, N, c.G)) continue;
+    const size_t base = (size_t)(w + b) * c.H + h;
+    const float wt = __builtin_amdgcn_exp2f(c.part_ml[base * 2] - M);
+    lsum += wt * c.part_ml[base * 2 + 1];
+    const float2 v = *(const float2*)(c.part_o + base * kLora + d);
+    acc0 += wt * v.x;
+    acc1 += wt * v.y;
   }
   const float inv = 1.f / lsum;
-  *(uint32_t*)(o_lat + ((long)b * H + h) * kLora + d) = pack_bf16x2(acc0 * inv, acc1 * inv);
+  // o_lat as a bf16 pair (hi + lo): the output projection runs on bf16 MFMA
+  // and takes both terms, so o_lat is not rounded to 8 bits on the way
+  const float v0 = acc0 * inv, v1 = acc1 * inv;
+  const uint32_t hi = pack_bf16x2(v0, v1);
+  const uint32_t lo = pack_bf16x2(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
+  uint16_t* orow = c.o_lat + ((size_t)b * c.H + h) * (2 * kLora);
+  *(uint32_t*)(orow + d) = hi;
+  *(uint32_t*)(orow + kLora + d) = lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -314,28 +547,32 @@ hipError_t launch_decode_absorb(void* q_abs, const uint16_t* q, const uint16_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.B * a.P), dim3(256), 0, stream, a);
+hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, B);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_combine(uint16_t* o_lat, const float* part_o, const float* part_ml,
-                                 const uint32_t* ctx, int B, int H, int P, int keys_per_part,
-                                 hipStream_t stream) {
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(B * H), dim3(256), 0, stream, o_lat, part_o,
-                     part_ml, ctx, H, P, keys_per_part);
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
+  const int grid = a.halves == 2 ? 16 * ((a.G + 7) / 8) : a.G;
+  hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(kDecThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const CombineArgs& c, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(c.B * c.H), dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_project(uint16_t* out, const uint16_t* o_lat, const uint16_t* w_uv,
                                  int B, int H, hipStream_t stream) {
-  // out[b, h, d] = sum_l o_lat[b, h, l] w_uv[h, d, l]: K = 512, N = 128
+  // out[b, h, d] = sum_l o_lat[b, h, l] w_uv[h, d, l]: K = 512, N = 128; o_lat
+  // rows hold hi then lo (2 x 512 bf16)
   const int ntn = kV / 32;
   const int tiles = ((B + 31) / 32) * ntn;
   const dim3 grid((tiles + 3) / 4, H);
-  hipLaunchKernelGGL((head_gemm_kernel<kLora, false>), grid, dim3(256), 0, stream, out, o_lat,
-                     w_uv, B, kV, (long)H * kLora, (long)kLora, (long)kV * kLora,
-                     (long)H * kV, (long)kV, ntn);
+  hipLaunchKernelGGL((head_gemm_kernel<kLora, false, true>), grid, dim3(256), 0, stream, out,
+                     o_lat, w_uv, B, kV, (long)H * 2 * kLora, (long)2 * kLora,
+                     (long)kV * kLora, (long)H * kV, (long)kV, ntn);
   return hipGetLastError();
 }
 

@@ -44,16 +44,26 @@ struct AttnArgs {
   float scale_log2;
 };
 struct DecodeArgs {
-  const uint16_t* q_abs;
-  const void* cache;
-  const int32_t* page_table;
-  const uint32_t* ctx;
-  float* part_o;
-  float* part_ml;
-  int B, H, ps, maxp, num_pages, P, keys_per_part;
+  const uint16_t* q_abs;     // [B][H][576] bf16
+  const void* cache;         // [num_pages][ps][576]
+  const int32_t* page_table; // [B][maxp]
+  const uint32_t* cum;       // [B+1] prefix sums of the context lengths
+  float* part_o;             // [G + B][H][512]
+  float* part_ml;            // [G + B][H][2]
+  int B, H, ps, maxp, num_pages, G, halves;
   float scale_log2;
 };
-
+struct CombineArgs {
+  uint16_t* o_lat;           // [B][H][2][512] bf16: hi then lo
+  float* part_o;             // [G + B][H][512]
+  float* part_ml;            // [G + B][H][2]; a negative sum marks a partial to recompute
+  const uint32_t* cum;       // [B+1]
+  const uint16_t* q_abs;     // [B][H][576]
+  const void* cache;
+  const int32_t* page_table;
+  int B, H, G, ps, maxp, num_pages;
+  float scale_log2;
+};
 hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,
                        const uint32_t*, int, int, uint32_t, hipStream_t);
 hipError_t launch_gather(const GatherArgs&, bool, bool, hipStream_t);
@@ -64,8 +74,8 @@ hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
 hipError_t launch_decode_absorb(void*, const uint16_t*, const uint16_t*, int, int, bool,
                                 hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, hipStream_t);
-hipError_t launch_decode_combine(uint16_t*, const float*, const float*, const uint32_t*, int,
-                                 int, int, int, hipStream_t);
+hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, hipStream_t);
+hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);
 }  // namespace mla

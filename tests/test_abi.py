@@ -52,7 +52,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     # max_rows not a multiple of 64
     assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
     # workspace too small
-    need = lib.mla_decode_workspace_size(4, 8, 1000, 0, 0)
+    need = lib.mla_decode_workspace_size(4, 8, 1000, 16, 0, 0)
     assert need > 0
     st = lib.mla_decode(fake, fake, fake, fake, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
                         0.1, fake, need - 1, None)

@@ -306,7 +306,7 @@ def _run_decode(B, wl, num_partitions=0):
     return _f64(out)
 
 
-@pytest.mark.parametrize("parts", [0, 1, 3])
+@pytest.mark.parametrize("parts", [0, 1, 3, 7])
 def test_decode_small_full(B, parts):
     wl = make_decode("d", 51, [1, 37, 300, 64, 1000], 8, 16)
     _assert_close(_run_decode(B, wl, parts), oracle.decode(wl), BF16_MAX, BF16_MEAN)
@@ -327,3 +327,23 @@ def test_decode_b64_sampled(B):
     ref = oracle.decode(wl, batch_indices=idx)
     assert np.isfinite(got).all()
     _assert_close(got[idx], ref, BF16_MAX, BF16_MEAN)
+
+
+@pytest.mark.parametrize("parts", [0, 1])
+def test_decode_extreme_score_range_recomputed(B, parts):
+    """One late cache row whose rope part is 16 * sign(q_rope) of head 0 (latent
+    part zero): its logit for head 0 exceeds the other rows' by ~80 log2 units,
+    more than the split kernel's 64-unit range, so with one key range (parts =
+    1; the row sits in the 19th tile of its segment) that partial is handed to
+    the combine step's recomputation; without it exp2 would overflow fp32. The
+    rope half of q enters the scores unrounded, so bf16 bounds apply as usual."""
+    wl = make_decode("ext", 61, [700, 300], 8, 16)
+    dec = oracle.DecodedDecode(wl)
+    row = np.zeros(576, dtype=np.float32)
+    row[512:] = 16.0 * np.sign(dec.q[0, 0, 128:])
+    p = 600  # position in sequence 0, well after its first tiles
+    slot = int(wl.page_table[0, p // wl.page_size]) * wl.page_size + p % wl.page_size
+    wl.pool.reshape(-1, 576)[slot] = f32_to_bf16_bits(row)
+    got = _run_decode(B, wl, parts)
+    ref = oracle.decode(wl)
+    _assert_close(got, ref, BF16_MAX, BF16_MEAN)
