@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_with_lane32(tmax);
     const float mt = tmax * sl2;
     const bool grow = mt > m_run + kRescaleSlack;
     if (__ballot(grow) != 0) {
@@ -319,7 +319,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
       }
       pb[ks] = __builtin_bit_cast(bf16x8, w);
     }
-    psum += __shfl_xor(psum, 32, 64);
+    psum = sum_with_lane32(psum);
     l_run += psum;
 
     // ---- O^T += V^T P^T ----

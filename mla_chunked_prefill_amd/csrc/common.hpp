@@ -87,4 +87,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Reductions of a value with the lane 32 away (v_permlane32_swap, gfx950): the
+// swap leaves lanes l < 32 holding (x[l], x[l+32]) and lanes l >= 32 holding
+// (x[l-32], x[l]) in its two results, so combining them pairs every lane with
+// its partner without a round trip through LDS.
+__device__ __forceinline__ float max_with_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace mla

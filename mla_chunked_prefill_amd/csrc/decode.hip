@@ -117,19 +117,26 @@ __global__ void copy_rope_kernel(void* __restrict__ q_abs, const uint16_t* __res
 // marks its partials invalid (with the exact maximum of the segment, which it
 // keeps tracking) and the combine step recomputes them.
 //
-// Tiles of 32 rows are triple-buffered in LDS by direct global->LDS loads; a
-// row occupies 73 16-byte chunks (72 + one pad chunk) so that reads of one
-// column across rows, and the transposed reads, hit distinct banks.
+// Tiles of 32 rows are triple-buffered in LDS by direct global->LDS loads. A
+// row keeps its 72 16-byte chunks with the chunk index's low three bits XORed
+// by zswz(row), which makes both the score-operand reads (16 rows at one
+// column) and the transposed reads (4 rows x 64 bytes) bank-conflict free.
+// Every LDS address the loop uses is a per-lane base plus an immediate.
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecHeads = 64;                     // heads per workgroup
 constexpr int kDecBN = 32;                        // rows per tile
-constexpr int kZRowChunks = 73;                   // 16-byte chunks per LDS row
-constexpr int kZRowB = kZRowChunks * 16;          // 1168 bytes
-constexpr int kZLoads = (kDecBN * kZRowChunks + 63) / 64;  // 37 wave loads of 1 KB
-constexpr int kZStageB = kZLoads * 1024;          // 37888 bytes
+constexpr int kZRowChunks = 72;                   // 16-byte chunks per row
+constexpr int kZRowB = kZRowChunks * 16;          // 1152 bytes
+constexpr int kZLoads = kDecBN * kZRowChunks / 64;  // 36 wave loads of 1 KB
+constexpr int kZStageB = kZLoads * 1024;          // 36864 bytes
 constexpr int kZStages = 3;
-constexpr int kDmaPerWave = (kZLoads + kDecWaves - 1) / kDecWaves;  // 10
+constexpr int kDmaPerWave = kZLoads / kDecWaves;  // 9
+static_assert(kZLoads % kDecWaves == 0, "every wave issues the same loads");
+
+// XOR applied to the low three bits of a row's 16-byte chunk index
+__device__ __forceinline__ int zswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
+__device__ __forceinline__ int zchunk(int row, int chunk) { return (chunk & ~7) | ((chunk & 7) ^ zswz(row)); }
 constexpr int kPTWindow = 2048;                   // page-table entries staged per segment
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
@@ -146,7 +153,9 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* lds_byte_ptr) {
 // lds_dst + 16 l (lds_dst is wave-uniform). Issued as inline assembly so that
 // the compiler does not treat later LDS reads of other stages as dependent on
 // it (it would wait for every load in flight); the kernel orders these loads
-// itself with s_waitcnt vmcnt, counting in issue order, and barriers.
+// itself with s_waitcnt vmcnt, counting in issue order, and barriers. The
+// asm sets m0 itself on every call; the compiler keeps no value of its own in
+// m0 in these kernels (checked in their assembly), so the clobber is safe.
 __device__ __forceinline__ void dma16(const void* src, uint8_t* lds_dst) {
   const uint32_t lds_addr = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds_dst);
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -182,16 +191,36 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
   const float sl2 = a.scale_log2;
   const uint16_t* cache = (const uint16_t*)a.cache;
 
-  // per-lane LDS byte offsets (within a stage)
+  // per-lane LDS byte offsets (within a stage). Scores: row kappa (bits 2 and 3
+  // of l32 swapped), chunk 36*dh + hf + 2*ks; ks = 4a + r -> s_base[r] + 128 a.
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  const int s_off = kappa * kZRowB + (36 * dh + hf) * 16;  // + 32 * ks
+  int s_base[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s_base[r] = kappa * kZRowB + zchunk(kappa, 36 * dh + hf + 2 * r) * 16;
+  // transposed reads for (ks, t): row 16*ks + 8*(g16/2) + 4*t + L16/4, bytes
+  // 512*dh + 64*md + 32*(g16&1) + 8*(L16&3); md = 2a + pm -> tr_base[ks][t][pm] + 128 a
   const int g16 = lane >> 4, L16 = lane & 15;
-  // transposed reads: row 16*ks + 8*(g16/2) + 4*t + L16/4, dims 256*dh + 32*md +
-  // 16*(g16&1) + 4*(L16&3)
-  const int tr_base = (8 * (g16 >> 1) + (L16 >> 2)) * kZRowB +
-                      (32 * dh + 2 * (g16 & 1) + ((L16 >> 1) & 1)) * 16 + (L16 & 1) * 8;
-  const int my_loads = (wave + kDecWaves * (kDmaPerWave - 1) < kZLoads) ? kDmaPerWave
-                                                                         : kDmaPerWave - 1;
+  int tr_base[2][2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int pm = 0; pm < 2; ++pm) {
+        const int row = 16 * ks + 8 * (g16 >> 1) + 4 * t + (L16 >> 2);
+        const int chunk = 32 * dh + 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
+        tr_base[ks][t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
+      }
+  // the DMA loads of this wave: j = wave + 4 i (i < 9) fills LDS chunks
+  // 64 j + lane; keep (tile row << 8 | source chunk) per load, two per register
+  int dma_rc[(kDmaPerWave + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int pch = (wave + kDecWaves * i) * 64 + lane;
+    const int row = pch / kZRowChunks;
+    const int rc = (row << 8) | zchunk(row, pch - row * kZRowChunks);  // XOR is its own inverse
+    if (i & 1) dma_rc[i >> 1] |= rc << 16; else dma_rc[i >> 1] = rc;
+  }
 
   // first sequence touched: largest b with cum[b] <= s_lo
   int b;
@@ -225,22 +254,15 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     auto issue = [&](int tile, int stage) {
       uint8_t* base = sZ + stage * kZStageB;
       const int kt = k0 + tile * kDecBN;
+      // pool row of tile row (lane & 31); rows past the segment read a valid row
+      const int key = min(kt + (lane & 31), k1 - 1);
+      const int lp = key / a.ps;
+      const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
 #pragma unroll
       for (int i = 0; i < kDmaPerWave; ++i) {
-        const int j = wave + kDecWaves * i;
-        if (j < kZLoads) {
-          // LDS chunk position p = 64 j + lane holds (row, col) of the tile; the
-          // pad chunk of a row and the tail of the last load fetch valid data
-          const int p = j * 64 + lane;
-          int row = p / kZRowChunks;
-          int col = p - row * kZRowChunks;
-          if (col == kZRowChunks - 1) col = 0;
-          if (row >= kDecBN) { row = kDecBN - 1; col = 0; }
-          const int key = min(kt + row, k1 - 1);  // rows past the segment: a valid row
-          const int lp = key / a.ps;
-          const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
-          dma16(cache + ((size_t)slot * kCache + col * 8), base + j * 1024);
-        }
+        const int rc = (dma_rc[i >> 1] >> (16 * (i & 1))) & 0xFFFF;
+        const int rs = __shfl(slot, rc >> 8, 64);
+        dma16(cache + ((size_t)rs * kCache + (rc & 255) * 8), base + (wave + kDecWaves * i) * 1024);
       }
     };
 
@@ -275,8 +297,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     for (int t = 0; t < ntiles; ++t) {
       // wait for this wave's loads of tile t (tile t+1's may stay in flight)
       if (t + 1 < ntiles) {
-        if (my_loads == kDmaPerWave) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // = kDmaPerWave
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
@@ -285,15 +306,19 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       const uint8_t* Z = sZ + (t % kZStages) * kZStageB;
       const int kt = k0 + t * kDecBN;
 
-      // partial scores over this wave's depth half
-      f32x16 s;
+      // partial scores over this wave's depth half, in two independent chains
+      f32x16 s, s2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+      for (int i = 0; i < 16; ++i) { s[i] = 0.f; s2[i] = 0.f; }
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8 za = *(const bf16x8*)(Z + s_off + 32 * ks);
+      for (int ks = 0; ks < 18; ks += 2) {
+        const bf16x8 za = *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
+        const bf16x8 zb = *(const bf16x8*)(Z + s_base[(ks + 1) & 3] + 128 * ((ks + 1) >> 2));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qf[ks], s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, qf[ks + 1], s2, 0, 0, 0);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] += s2[i];
       float* xw = sX + wave * 1024;
 #pragma unroll
       for (int i = 0; i < 16; ++i) xw[i * 64 + lane] = s[i];
@@ -311,7 +336,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       float tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_with_lane32(tmax);
       const float mt = tmax * sl2;  // finite: every tile holds a valid row
       m_seen = fmaxf(m_seen, mt);
       if (m_ref == -INFINITY) m_ref = mt;
@@ -331,7 +356,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         }
         pb[ks] = __builtin_bit_cast(bf16x8, wv);
       }
-      psum += __shfl_xor(psum, 32, 64);
+      psum = sum_with_lane32(psum);
       l_run += psum;
 
       // O^T[256 dims x 32 heads] += Z^T P^T, Z^T read transposed from the row tile
@@ -339,8 +364,8 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       for (int md = 0; md < 8; ++md)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const bf16x4 a0 = ds_read_tr16(Z + tr_base + 16 * ks * kZRowB + 64 * md);
-          const bf16x4 a1 = ds_read_tr16(Z + tr_base + (16 * ks + 4) * kZRowB + 64 * md);
+          const bf16x4 a0 = ds_read_tr16(Z + tr_base[ks][0][md & 1] + 128 * (md >> 1));
+          const bf16x4 a1 = ds_read_tr16(Z + tr_base[ks][1][md & 1] + 128 * (md >> 1));
           const bf16x8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
           o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
         }
