@@ -6,8 +6,17 @@
 // Work decomposition. A workgroup (4 waves, 256 threads) owns one block of 128
 // queries of one sequence and one head; each wave owns 32 of the queries.
 // Keys are streamed in tiles of 64 rows aligned to the chunk buffer's 64-row
-// grid (so every global load is 16-byte aligned); rows that belong to other
-// sequences are masked.
+// grid; rows that belong to other sequences are masked.
+//
+// Tile movement. Every tile (K_nope, the shared k_rope rows and the value
+// tile V^T) goes from global memory straight into LDS with 16-byte direct
+// loads (global_load_lds_dwordx4): each lane's source offset inside a tile is
+// fixed for the whole kernel, only the scalar tile base changes, so a tile
+// costs ten load instructions per wave and no vector ALU work. Two LDS stages
+// alternate: while a wave computes on tile t, the loads of tile t+1 fill the
+// other stage, and one barrier per tile separates the two uses of a stage.
+// Within a stage every row's 16-byte chunks are XOR-permuted by a function of
+// the row so that the operand reads below hit distinct LDS banks.
 //
 // MFMA orientation. Scores are computed transposed, S^T = K Q^T, on
 // mfma 32x32x16: rows are keys, columns are queries, so each lane owns one
@@ -19,23 +28,21 @@
 // value product O^T += V^T P^T, whose A operand reads 8 consecutive keys of the
 // transposed value tile from LDS with one 16-byte load.
 //
-// The k_rope tile (one head shared by all query heads) sits beside K_nope in
-// the same LDS row, so the 192-deep score reduction is 12 MFMA steps.
+// The k_rope tile (one head shared by all query heads) is read next to K_nope,
+// so the 192-deep score reduction is 12 MFMA steps of 16.
 //
 // Softmax runs online in the log2 domain (scale * log2(e) folded into one
 // multiply). Its state (max, sum, unnormalised output) is carried across the
 // chunks of a sequence through the workspace; a query's output is written in
 // the chunk that holds its last visible key.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace mla {
 
-constexpr int kAttnBM = 128;           // queries per workgroup
-constexpr int kAttnBN = 64;            // keys per tile
-constexpr int kKRowBf16 = kQDepth + 8; // LDS K row, bf16 elements (400 B)
-constexpr int kKRowFp8 = kQDepth + 16; // LDS K row, bytes (208 B)
-constexpr int kVRow = kAttnBN + 8;     // LDS V^T row, bf16 elements (144 B)
-
+constexpr int kAttnBM = 128;  // queries per workgroup
+constexpr int kAttnBN = 64;   // keys per tile
 
 typedef long fp8x8;  // 8 e4m3 values in one 64-bit register pair
 
@@ -44,116 +51,73 @@ typedef long fp8x8;  // 8 e4m3 values in one 64-bit register pair
 // against the stale maximum and stay below 2^8, exact in fp32 and bf16 range.
 constexpr float kRescaleSlack = 8.0f;
 
-// Per-thread staging registers of one key tile (global -> registers -> LDS).
+// LDS layout of one stage: K_nope rows, k_rope rows, then V^T (128 dims x 64
+// keys). Row sizes in bytes; every region is a whole number of 4 KB (one 1 KB
+// direct load per wave).
 template <bool kFp8>
-struct TileRegs;
-template <>
-struct TileRegs<false> {
-  u32x4 kn[4], kr[2], v[4];
-};
-template <>
-struct TileRegs<true> {
-  u32x4 kn[2], kr[1], v[4];
+struct AttnStage {
+  static constexpr int kNopeRowB = kFp8 ? kNope : 2 * kNope;  // 128 / 256
+  static constexpr int kRopeRowB = kFp8 ? kRope : 2 * kRope;  // 64 / 128
+  static constexpr int kVRowB = 2 * kAttnBN;                  // 128
+  static constexpr int kNopeB = kAttnBN * kNopeRowB;
+  static constexpr int kRopeB = kAttnBN * kRopeRowB;
+  static constexpr int kVB = kV * kVRowB;
+  static constexpr int kRopeOff = kNopeB;
+  static constexpr int kVOff = kNopeB + kRopeB;
+  static constexpr int kBytes = kNopeB + kRopeB + kVB;
+  static constexpr int kNopeLoads = kNopeB / 4096;  // per wave
+  static constexpr int kRopeLoads = kRopeB / 4096;
+  static constexpr int kVLoads = kVB / 4096;
+  static constexpr int kLoads = kNopeLoads + kRopeLoads + kVLoads;
 };
 
-template <bool kFp8>
-__device__ __forceinline__ void load_tile(TileRegs<kFp8>& R, const AttnArgs& a, int h, int tb,
-                                          int r0, int len, int tid) {
-  const int lo = max(r0, 0);
-  const int hi = min(r0 + len, a.max_rows);
-  const bool full = tb >= lo && tb + kAttnBN <= hi;  // uniform across the workgroup
-  const size_t kbase = (size_t)h * a.max_rows;
-  if (kFp8) {
-    const uint8_t* kn = (const uint8_t*)a.k_nope;
-    const uint8_t* kr = (const uint8_t*)a.krope;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;
-      const int gr = tb + (c >> 3);
-      const bool ok = full || (gr >= lo && gr < hi);
-      R.kn[it] = ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + (c & 7) * 16) : u32x4{0, 0, 0, 0};
-    }
-    {
-      const int gr = tb + (tid >> 2);
-      const bool ok = full || (gr >= lo && gr < hi);
-      ((u32x4*)R.kr)[0] = ok ? *(const u32x4*)(kr + (size_t)gr * kRope + (tid & 3) * 16)
-                             : u32x4{0, 0, 0, 0};
-    }
-  } else {
-    const uint16_t* kn = (const uint16_t*)a.k_nope;
-    const uint16_t* kr = (const uint16_t*)a.krope;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid + it * 256;
-      const int gr = tb + (c >> 4);
-      const bool ok = full || (gr >= lo && gr < hi);
-      ((u32x4*)R.kn)[it] =
-          ok ? *(const u32x4*)(kn + (kbase + gr) * kNope + (c & 15) * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;
-      const int gr = tb + (c >> 3);
-      const bool ok = full || (gr >= lo && gr < hi);
-      ((u32x4*)R.kr)[it] =
-          ok ? *(const u32x4*)(kr + (size_t)gr * kRope + (c & 7) * 8) : u32x4{0, 0, 0, 0};
-    }
-  }
-  const uint16_t* vbase = a.v_t + (size_t)h * kV * a.max_rows;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {  // V^T: 128 dims x 8 chunks of 8 keys
-    const int c = tid + it * 256;
-    const int k0 = tb + (c & 7) * 8;
-    u32x4 v = *(const u32x4*)(vbase + (size_t)(c >> 3) * a.max_rows + k0);
-    if (!full && (k0 < lo || k0 + 8 > hi)) {  // zero keys outside this sequence
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ka = k0 + 2 * j;
-        uint32_t w = v[j];
-        if (ka < lo || ka >= hi) w &= 0xFFFF0000u;
-        if (ka + 1 < lo || ka + 1 >= hi) w &= 0x0000FFFFu;
-        v[j] = w;
-      }
-    }
-    R.v[it] = v;
-  }
+// Chunk permutations (XOR on the low chunk-index bits, so a row's chunks stay
+// in the row). With rows fed in the order kappa(lane) the score reads of any
+// 8 or 16 consecutive lanes touch distinct 16-byte bank groups of a 128- or
+// 256-byte LDS line, and so do the value reads (rows in lane order).
+__device__ __forceinline__ int swz3(int r) { return ((r & 3) | ((r >> 1) & 4)) ^ ((r >> 2) & 1); }
+__device__ __forceinline__ int swz4(int r) { return swz3(r) | ((r << 1) & 8); }
+__device__ __forceinline__ int swzv(int d) { return (d & 7) ^ ((d >> 3) & 1); }
+template <int kChunks>
+__device__ __forceinline__ int swz_rows(int r) {
+  return kChunks >= 16 ? swz4(r) : (kChunks == 8 ? swz3(r) : (swz3(r) & 3));
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void store_tile(const TileRegs<kFp8>& R, uint8_t* sK, uint16_t* sV,
-                                           int tid) {
-  if (kFp8) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;
-      *(u32x4*)(sK + (c >> 3) * kKRowFp8 + (c & 7) * 16) = R.kn[it];
-    }
-    *(u32x4*)(sK + (tid >> 2) * kKRowFp8 + kNope + (tid & 3) * 16) = ((const u32x4*)R.kr)[0];
-  } else {
-    uint16_t* k16 = (uint16_t*)sK;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = tid + it * 256;
-      *(u32x4*)(k16 + (c >> 4) * kKRowBf16 + (c & 15) * 8) = ((const u32x4*)R.kn)[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = tid + it * 256;
-      *(u32x4*)(k16 + (c >> 3) * kKRowBf16 + kNope + (c & 7) * 8) = ((const u32x4*)R.kr)[it];
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int c = tid + it * 256;
-    *(u32x4*)(sV + (c >> 3) * kVRow + (c & 7) * 8) = R.v[it];
-  }
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes, read from
+// sbase + voff, land at LDS byte address lds + 16 l (lds and sbase are
+// wave-uniform). Inline assembly keeps the compiler from treating later LDS
+// reads as dependent on it (it would wait for every load in flight); the
+// kernel orders these loads itself with s_waitcnt vmcnt and barriers. The asm
+// sets m0 on every call; the kernels keep no value of their own in m0.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Per-lane source offset (bytes, inside a tile) of direct load `i` of a region
+// whose LDS rows hold kChunks 16-byte chunks and whose global rows are
+// `gstride` bytes apart (kValue: the value tile's permutation).
+template <int kChunks, bool kValue = false>
+__device__ __forceinline__ uint32_t dma_src(int i, int lane, uint32_t gstride) {
+  const int p = i * 64 + lane;
+  const int r = p / kChunks;
+  const int j = (p % kChunks) ^ (kValue ? swzv(r) : swz_rows<kChunks>(r));
+  return (uint32_t)r * gstride + (uint32_t)j * 16u;
 }
 
 template <bool kFp8>
 __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
-  constexpr int kKBytes = kFp8 ? kAttnBN * kKRowFp8 : kAttnBN * kKRowBf16 * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t sK[kKBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kV * kVRow];
+  using L = AttnStage<kFp8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * L::kBytes];
 
   // XCD-aware order: consecutive workgroups of one XCD share a head.
   const int total = a.n_slots * a.H;
@@ -180,12 +144,11 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   if (len <= 0 || q_lo >= n_b) return;
   const int P_hi = c_b + q_hi - 1;
   if (co > P_hi) return;
-  const int kv_end = min(len, P_hi - co + 1);             // keys j < kv_end can be visible
-  const int all_vis = min(len, c_b + q_lo - co + 1);      // keys j < all_vis visible to all
+  const int kv_end = min(len, P_hi - co + 1);  // keys j < kv_end can be visible
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -196,7 +159,12 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   const size_t t = (size_t)t0 + qi;
   // visible buffer rows of this query: [r0, r_hi]
   const int r_hi = active ? r0 + min(len - 1, P - co) : r0 - 1;
-  const bool wave_active = __ballot(active) != 0;
+  // wave-uniform bounds: rows every valid query of the wave sees, and rows any sees
+  const int wq_lo = q_lo + wave * 32;
+  const int wq_hi = min(wq_lo + 32, n_b);  // exclusive
+  const bool wave_active = wq_lo < n_b && c_b + wq_hi - 1 >= co;
+  const int w_all_hi = r0 + min(len - 1, c_b + wq_lo - co);     // may be < r0
+  const int w_any_hi = r0 + min(len - 1, c_b + wq_hi - 1 - co);
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, depth 8*hf + 16*ks ..)
   bf16x8 qf[12];
@@ -235,23 +203,73 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     l_run = a.carry_ml[(t * a.H + h) * 2 + 1];
   }
 
-  // permuted K row fed by this lane: swap bits 2 and 3 of l32
+  // ---- per-lane LDS read offsets (bytes inside a stage) ----
+  // permuted K row fed by this lane: bits 2 and 3 of l32 swapped
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  const float sl2 = a.scale_log2;
+  constexpr int kNopeC = L::kNopeRowB / 16;
+  constexpr int kRopeC = L::kRopeRowB / 16;
+  int nb[8], rb[4], vb[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kFp8) nb[kk] = kappa * L::kNopeRowB + ((kk ^ swz_rows<kNopeC>(kappa)) * 16) + hf * 8;
+    else nb[kk] = kappa * L::kNopeRowB + (((2 * kk + hf) ^ swz_rows<kNopeC>(kappa)) * 16);
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (kFp8)
+      rb[kk] = L::kRopeOff + kappa * L::kRopeRowB + ((kk ^ swz_rows<kRopeC>(kappa)) * 16) + hf * 8;
+    else
+      rb[kk] = L::kRopeOff + kappa * L::kRopeRowB + (((2 * kk + hf) ^ swz_rows<kRopeC>(kappa)) * 16);
+    vb[kk] = L::kVOff + l32 * L::kVRowB + (((2 * kk + hf) ^ swzv(l32)) * 16);
+  }
 
+  // ---- per-lane direct-load source offsets (bytes inside a tile) ----
+  uint32_t src_n[L::kNopeLoads], src_r[L::kRopeLoads], src_v[L::kVLoads];
+#pragma unroll
+  for (int k = 0; k < L::kNopeLoads; ++k)
+    src_n[k] = dma_src<kNopeC>(wave + 4 * k, lane, L::kNopeRowB);
+#pragma unroll
+  for (int k = 0; k < L::kRopeLoads; ++k)
+    src_r[k] = dma_src<kRopeC>(wave + 4 * k, lane, L::kRopeRowB);
+#pragma unroll
+  for (int k = 0; k < L::kVLoads; ++k)
+    src_v[k] = dma_src<8, true>(wave + 4 * k, lane, (uint32_t)a.max_rows * 2u);
+
+  const uint8_t* kn_head = (const uint8_t*)a.k_nope + (size_t)h * a.max_rows * L::kNopeRowB;
+  const uint8_t* kr_base = (const uint8_t*)a.krope;
+  const uint8_t* v_head = (const uint8_t*)a.v_t + (size_t)h * kV * a.max_rows * 2;
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)smem);
+
+  auto issue = [&](int tb, int stage) {
+    const uint32_t base = lds0 + stage * L::kBytes;
+    const void* sn = uniform_ptr(kn_head + (size_t)tb * L::kNopeRowB);
+    const void* sr = uniform_ptr(kr_base + (size_t)tb * L::kRopeRowB);
+    const void* sv = uniform_ptr(v_head + (size_t)tb * 2);
+#pragma unroll
+    for (int k = 0; k < L::kNopeLoads; ++k)
+      dma16(sn, src_n[k], base + (wave + 4 * k) * 1024);
+#pragma unroll
+    for (int k = 0; k < L::kRopeLoads; ++k)
+      dma16(sr, src_r[k], base + L::kRopeOff + (wave + 4 * k) * 1024);
+#pragma unroll
+    for (int k = 0; k < L::kVLoads; ++k)
+      dma16(sv, src_v[k], base + L::kVOff + (wave + 4 * k) * 1024);
+  };
+
+  const float sl2 = a.scale_log2;
   const int tile_begin = r0 & ~(kAttnBN - 1);
   // never past the buffer, even if a caller's max_rows is smaller than the chunk
   const int tile_end = min(r0 + kv_end, a.max_rows);
+  const int n_tiles = tile_end > tile_begin ? (tile_end - tile_begin + kAttnBN - 1) / kAttnBN : 0;
 
-  TileRegs<kFp8> R;
-  if (tile_begin < tile_end) load_tile<kFp8>(R, a, h, tile_begin, r0, len, tid);
-
-  for (int tb = tile_begin; tb < tile_end; tb += kAttnBN) {
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile<kFp8>(R, sK, sV, tid);
-    __syncthreads();
-    if (tb + kAttnBN < tile_end) load_tile<kFp8>(R, a, h, tb + kAttnBN, r0, len, tid);
-    if (!wave_active) continue;
+  auto body = [&](auto stage_c, int tt) {
+    constexpr int S = decltype(stage_c)::value;
+    const int tb = tile_begin + tt * kAttnBN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile tt landed for every wave; the other stage is free
+    if (tt + 1 < n_tiles) issue(tb + kAttnBN, S ^ 1);
+    if (!wave_active || tb > w_any_hi) return;
+    const uint8_t* st = smem + S * L::kBytes;
 
     // ---- S^T = K Q^T for 64 keys x 32 queries ----
     f32x16 s[2];
@@ -263,12 +281,13 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < 12; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
+        const int off = ks < 8 ? nb[ks] + mb * 32 * L::kNopeRowB
+                               : rb[ks - 8] + mb * 32 * L::kRopeRowB;
         if (kFp8) {
-          const fp8x8 ka = *(const fp8x8*)(sK + (mb * 32 + kappa) * kKRowFp8 + ks * 16 + hf * 8);
+          const fp8x8 ka = *(const fp8x8*)(st + off);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ka, qf8[ks], s[mb], 0, 0, 0);
         } else {
-          const bf16x8 ka = *(const bf16x8*)((const uint16_t*)sK +
-                                             (mb * 32 + kappa) * kKRowBf16 + ks * 16 + hf * 8);
+          const bf16x8 ka = *(const bf16x8*)(st + off);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[mb], 0, 0, 0);
         }
       }
@@ -276,7 +295,7 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
 
     // ---- online softmax (log2 domain), lazily rescaled ----
     // register i of block mb holds the key at tile row 32*mb + 16*(i/8) + 8*hf + i%8
-    if ((tb < r0) || (tb + kAttnBN > r0 + all_vis)) {
+    if (tb < r0 || tb + kAttnBN - 1 > w_all_hi) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -327,10 +346,22 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int md = 0; md < 4; ++md) {
-        const bf16x8 va = *(const bf16x8*)(sV + (md * 32 + l32) * kVRow + ks * 16 + hf * 8);
+        const bf16x8 va = *(const bf16x8*)(st + vb[ks] + md * 32 * L::kVRowB);
         o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
       }
     }
+  };
+
+  // q and the carry are in registers before any tile load is in flight, so
+  // the waits of the tile loop count only tile loads. The builtin (gfx9
+  // encoding: vmcnt 0, other counters unlimited) tells the compiler that its
+  // own loads are complete; otherwise it would wait for them, and with them
+  // for the tile loads it cannot see, inside the loop.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (n_tiles > 0) issue(tile_begin, 0);
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    body(std::integral_constant<int, 0>(), tt);
+    if (tt + 1 < n_tiles) body(std::integral_constant<int, 1>(), tt + 1);
   }
 
   if (!active) return;
