@@ -56,11 +56,13 @@ class MlaError(RuntimeError):
         self.status = status
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmla.so once; raise if it has not been built."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmla.so once; raise if it has not been built. The MLA_LIB
+    environment variable names another build of the library to load."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("MLA_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m mla_chunked_prefill_amd.build`")

@@ -85,9 +85,6 @@ PrefillWs prefill_ws_layout(char* base, int B, int total_q, int H, int max_rows,
   return w;
 }
 
-// decode workspace: q_abs [B][H][576], cum [B+1] u32, part_o [G+B][H][512] f32,
-// part_ml [G+B][H][2] f32, o_lat [B][H][2][512] bf16 (hi, lo). G split workgroups cover
-// the batch's concatenated contexts in equal ranges.
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -99,20 +96,28 @@ int device_cu_count() {
   return n;
 }
 
-// Split workgroups over the batch. Each one's key range must span at most
-// 2046 pages (the page-table window it stages in LDS).
+// Split workgroups over the batch: one per compute unit by default. Each
+// one's key range must span at most 1022 pages (the page-table window it
+// stages in LDS holds 1024 entries; a range may start mid-page and its first
+// tile is aligned down to 32 keys).
 int decode_groups(int B, int max_ctx, int page_size, int num_partitions) {
   int g = num_partitions > 0 ? num_partitions : device_cu_count();
   const long long keys = (long long)B * max_ctx;
-  const long long per_group = 2046LL * page_size - 1;
+  const long long per_group = 1022LL * page_size - 64;
   const long long need = (keys + per_group - 1) / per_group;
   if (g < need) g = (int)need;
   return g;
 }
 
+// decode workspace: q_abs [B][H][576], cum [B+1] u32, wstart [G+1] u32,
+// wspan [B] int2, part_o [G+B][H][512] f32, part_ml [G+B][H][2] f32, o_lat
+// [B][H][2][512] bf16 (hi, lo). G split workgroups cover the batch's
+// concatenated contexts in equal ranges.
 struct DecodeWs {
   void* q_abs;
   uint32_t* cum;
+  uint32_t* wstart;
+  int2* wspan;
   float* part_o;
   float* part_ml;
   uint16_t* o_lat;
@@ -129,12 +134,16 @@ DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
   off = align_up(off + (size_t)B * H * mla::kCache * dsize(cache_dtype));
   w.cum = (uint32_t*)(base + off);
   off = align_up(off + (size_t)(B + 1) * sizeof(uint32_t));
+  w.wstart = (uint32_t*)(base + off);
+  off = align_up(off + (size_t)(w.G + 1) * sizeof(uint32_t));
+  w.wspan = (int2*)(base + off);
+  off = align_up(off + (size_t)B * sizeof(int2));
   w.part_o = (float*)(base + off);
   off = align_up(off + slots * H * mla::kLora * sizeof(float));
   w.part_ml = (float*)(base + off);
   off = align_up(off + slots * H * 2 * sizeof(float));
   w.o_lat = (uint16_t*)(base + off);
-  off = align_up(off + (size_t)B * H * 2 * mla::kLora * 2);  // hi and lo
+  off = align_up(off + (size_t)B * H * 2 * mla::kLora * 2);
   w.bytes = off;
   return w;
 }
@@ -399,7 +408,8 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                                                 fp8, stream),
                       "absorb kernel");
   if (st != MLA_OK) return st;
-  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, stream),
+  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, ws.wstart,
+                                            ws.wspan, ws.G, stream),
                   "prefix kernel");
   if (st != MLA_OK) return st;
   mla::DecodeArgs a;
@@ -407,6 +417,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   a.cache = kv_cache;
   a.page_table = page_table;
   a.cum = ws.cum;
+  a.wstart = ws.wstart;
   a.part_o = ws.part_o;
   a.part_ml = ws.part_ml;
   a.B = batch_size;
@@ -415,7 +426,6 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   a.maxp = max_pages_per_seq;
   a.num_pages = num_pages;
   a.G = ws.G;
-  a.halves = num_heads > 64 ? 2 : 1;
   a.scale_log2 = scale * kLog2e;
   st = hip_status(mla::launch_decode_split(a, stream), "split-KV kernel");
   if (st != MLA_OK) return st;
@@ -424,6 +434,8 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   c.part_o = ws.part_o;
   c.part_ml = ws.part_ml;
   c.cum = ws.cum;
+  c.wstart = ws.wstart;
+  c.wspan = ws.wspan;
   c.q_abs = (const uint16_t*)ws.q_abs;
   c.cache = kv_cache;
   c.page_table = page_table;

@@ -2,22 +2,17 @@
 // Args "w_uk" [H, 512, 128] and "w_uv" [H, 128, 512], num_partitions;
 // "flare_mla_prefill_dispatch" page: kv_num_heads 1, cache_depth 576).
 //
-// Four kernels:
+// Four steps:
 //  1. absorb:   q_abs[b, h] = [w_uk[h] q_nope[b, h] | q_rope[b, h]] (576 wide),
 //               bf16 MFMA, one wave per 32x32 output tile, operands read
 //               straight from global memory (both are contiguous along the
 //               128-long reduction).
-//  2. split-KV: one workgroup per (sequence, partition) streams the
-//               partition's 576-wide cache rows once for all heads. Each of the
-//               four waves keeps the absorbed queries of 32 heads in registers
-//               and computes S^T = Z Q^T (keys x heads) on mfma 32x32x16, so
-//               softmax statistics are per-lane. The tile is staged in LDS
-//               twice: row-major for the score product and transposed
-//               (512 x keys, built with an in-register 8x8 transpose) for the
-//               value product O^T += Z^T P^T, whose B operand is the
-//               bf16-converted score registers (K rows fed in the same
-//               bit-2/3-swapped order as the prefill kernel).
-//  3. combine:  log-sum-exp merge of the partitions' (max, sum, O) states.
+//  2. split-KV: the batch's contexts laid end to end are cut into G equal key
+//               ranges; one workgroup per range streams its 576-wide cache
+//               rows once for all 128 heads and keeps an unnormalised
+//               softmax state (max, sum, O_lat) per sequence it touches.
+//  3. combine:  per (sequence, head), the states of the key ranges that
+//               touched the sequence are merged by log-sum-exp into o_lat.
 //  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA like the absorb.
 #include "kernels.hpp"
 
@@ -26,7 +21,7 @@ namespace mla {
 typedef long fp8x8_d;
 
 // ---------------------------------------------------------------------------
-// 1/4. per-head small GEMMs: C[b, n] = sum_k X[b, k] W[n, k]
+// 1, 4. per-head small GEMMs: C[b, n] = sum_k X[b, k] W[n, k]
 // ---------------------------------------------------------------------------
 // X rows: x + b*x_stride (K contiguous, bf16); W rows: w + n*K (K contiguous).
 // Output: y[b*y_stride + n] as bf16 (or e4m3 when kFp8Out). One wave computes a
@@ -93,51 +88,67 @@ __global__ void copy_rope_kernel(void* __restrict__ q_abs, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// 2. balanced split-KV attention over the latent cache (bf16 cache)
+// 2. split-KV attention over the latent cache (bf16 cache)
 // ---------------------------------------------------------------------------
-// The batch's contexts are laid end to end (N keys in all) and key range w of G
-// covers keys [w*N/G, (w+1)*N/G): every range streams the same number of rows
+// Key ranges. The contexts laid end to end hold N keys; range w of G covers
+// keys [w*N/G, (w+1)*N/G), so every range streams the same number of rows
 // whatever the mix of context lengths. A range writes one partial state per
 // sequence it touches, into slot w + b (injective over the touching pairs, at
 // most G + B slots).
 //
-// Two workgroups share a range, one per half of the heads (64 each); they are
-// numbered so that both land on the same XCD back to back and the second read
-// of every tile hits that XCD's L2. A workgroup has four waves, one per SIMD:
-// head group hg = wave & 1 (32 heads) and half dh = wave >> 1. For the scores
-// S^T = Z Q^T (keys x heads, mfma 32x32x16: per-lane softmax statistics) a wave
-// reduces its 288 of the 576 depths and the two waves of a head group add their
-// partial score tiles through LDS; for the values O^T += Z^T P^T a wave keeps
-// its 256 of the 512 latent dims, reading Z^T straight from the row-major tile
-// with transposed LDS reads.
+// One workgroup per range, four waves, one per SIMD; wave w owns heads
+// 32w .. 32w+31 completely: its absorbed queries (576 deep) stay in registers
+// and so does its unnormalised output O^T (512 dims x 32 heads, fp32), so no
+// score or output crosses between waves and each cache row is read from
+// memory once for all heads. Per tile of 32 keys a wave computes the scores
+// S^T = Z Q^T (keys x heads, 36 MFMA steps, mfma 32x32x16: each lane owns
+// one head and its softmax statistics are in-lane plus one exchange with the
+// lane 32 away) and accumulates O^T += Z^T P^T (16 dim blocks x 2 key steps),
+// reading Z^T straight from the row-major tile with transposed LDS reads.
+// Key rows are fed to the score MFMA in the order kappa (bits 2 and 3 of the
+// row index swapped), which makes the bf16 probabilities directly the B
+// operand of the value product.
 //
-// The accumulator is never rescaled: each lane takes its first tile's maximum
-// as the reference and later probabilities are formed against it (exact in
-// bf16 and fp32 while below 2^64). A wave whose scores would exceed that
-// marks its partials invalid (with the exact maximum of the segment, which it
-// keeps tracking) and the combine step recomputes them.
+// The softmax reference maximum of a segment is its first tile's maximum and
+// never moves, so the output accumulator is never rescaled. Probabilities
+// stay below 2^kDecSlack (far inside fp32 and bf16 range) unless a later
+// score exceeds the reference by more than kDecSlack log2 units; a wave that
+// sees one marks its partial states, and the combine step recomputes them
+// against their exact maximum.
 //
-// Tiles of 32 rows are triple-buffered in LDS by direct global->LDS loads. A
-// row keeps its 72 16-byte chunks with the chunk index's low three bits XORed
-// by zswz(row), which makes both the score-operand reads (16 rows at one
-// column) and the transposed reads (4 rows x 64 bytes) bank-conflict free.
-// Every LDS address the loop uses is a per-lane base plus an immediate.
+// Tiles are aligned to 32 keys of the sequence (keys of the first tile before
+// the range start are masked). When the page size is a multiple of 32 a tile
+// is 32 consecutive pool rows (36 KB in one piece) and its direct loads use
+// per-lane offsets fixed for the whole kernel; otherwise every row's pool slot
+// is looked up. Two LDS stages keep one tile in flight while another is
+// computed (a tile's compute outlasts the memory latency). The first 18 score
+// steps take the absorbed queries from registers, the last 18 from a table in
+// LDS (registers hold the output accumulator instead). A row keeps its 72
+// 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
+// the score reads (16 rows at one column) and the transposed reads (4 rows x
+// 64 bytes) touch distinct LDS banks.
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecHeads = 64;                     // heads per workgroup
-constexpr int kDecBN = 32;                        // rows per tile
-constexpr int kZRowChunks = 72;                   // 16-byte chunks per row
-constexpr int kZRowB = kZRowChunks * 16;          // 1152 bytes
-constexpr int kZLoads = kDecBN * kZRowChunks / 64;  // 36 wave loads of 1 KB
-constexpr int kZStageB = kZLoads * 1024;          // 36864 bytes
-constexpr int kZStages = 3;
-constexpr int kDmaPerWave = kZLoads / kDecWaves;  // 9
+constexpr int kDecBN = 32;                          // keys per tile
+constexpr int kZRowChunks = 72;                     // 16-byte chunks per row
+constexpr int kZRowB = kZRowChunks * 16;            // 1152 bytes
+constexpr int kZStageB = kDecBN * kZRowB;           // 36864 bytes
+constexpr int kZStages = 2;
+constexpr int kZLoads = kZStageB / 1024;            // 36 wave loads of 1 KB
+constexpr int kDmaPerWave = kZLoads / kDecWaves;    // 9
+constexpr int kPTWindow = 1024;                     // page-table entries staged per segment
+// the second half of every absorbed query (depth 288 .. 575) lives in LDS:
+// rows of 288 bf16 + 16 bytes (spreads consecutive heads over distinct banks)
+constexpr int kQLdsSteps = 18;                      // score steps whose B operand is in LDS
+constexpr int kQRegSteps = 36 - kQLdsSteps;
+constexpr int kQRowB = kQLdsSteps * 32 + 16;        // 592 bytes
+constexpr int kQTabB = 128 * kQRowB;
+constexpr float kDecSlack = 64.0f;
 static_assert(kZLoads % kDecWaves == 0, "every wave issues the same loads");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
 __device__ __forceinline__ int zswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 __device__ __forceinline__ int zchunk(int row, int chunk) { return (chunk & ~7) | ((chunk & 7) ^ zswz(row)); }
-constexpr int kPTWindow = 2048;                   // page-table entries staged per segment
 
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
@@ -150,55 +161,62 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* lds_byte_ptr) {
 }
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
-// lds_dst + 16 l (lds_dst is wave-uniform). Issued as inline assembly so that
-// the compiler does not treat later LDS reads of other stages as dependent on
-// it (it would wait for every load in flight); the kernel orders these loads
-// itself with s_waitcnt vmcnt, counting in issue order, and barriers. The
-// asm sets m0 itself on every call; the compiler keeps no value of its own in
-// m0 in these kernels (checked in their assembly), so the clobber is safe.
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_dst) {
-  const uint32_t lds_addr = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds_dst);
+// lds + 16 l (lds is wave-uniform). Inline assembly keeps the compiler from
+// treating later LDS reads of other stages as dependent on it (it would wait
+// for every load in flight); the kernel orders these loads itself with
+// s_waitcnt vmcnt, counting in issue order, and barriers. The asm sets m0 on
+// every call; the kernels keep no value of their own in m0.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(src)
+               : "s"(lds), "v"(src)
                : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ const void* uniform_ptr_d(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
-  __shared__ __attribute__((aligned(16))) float sX[kDecWaves * 16 * 64];
+  // second half of the absorbed queries (B operand of the last 18 score steps)
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[kQTabB];
   __shared__ int sPT[kPTWindow];
 
-  // workgroup -> (key range, head half); the two halves of a range share an XCD
-  const int L = blockIdx.x;
-  const int w = a.halves == 2 ? (L >> 4) * 8 + (L & 7) : L;
-  const int half = a.halves == 2 ? (L >> 3) & 1 : 0;
+  const int w = blockIdx.x;
   if (w >= a.G) return;
-  const uint32_t N = a.cum[a.B];
-  const uint32_t s_lo = (uint32_t)(((uint64_t)w * N) / a.G);
-  const uint32_t s_hi = (uint32_t)(((uint64_t)(w + 1) * N) / a.G);
+  const uint32_t s_lo = a.wstart[w];
+  const uint32_t s_hi = a.wstart[w + 1];
   if (s_lo >= s_hi) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave & 1;
-  const int dh = wave >> 1;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int head = half * kDecHeads + hg * 32 + l32;
+  const int head = wave * 32 + l32;
   const bool hvalid = head < a.H;
   const float sl2 = a.scale_log2;
-  const uint16_t* cache = (const uint16_t*)a.cache;
+  const uint8_t* cache = (const uint8_t*)a.cache;
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)sZ);
 
-  // per-lane LDS byte offsets (within a stage). Scores: row kappa (bits 2 and 3
-  // of l32 swapped), chunk 36*dh + hf + 2*ks; ks = 4a + r -> s_base[r] + 128 a.
+  // ---- per-lane LDS read offsets (bytes inside a stage) ----
+  // scores: row kappa, chunk hf + 2 ks; ks = 4c + r -> s_base[r] + 128 c
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   int s_base[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s_base[r] = kappa * kZRowB + zchunk(kappa, 36 * dh + hf + 2 * r) * 16;
-  // transposed reads for (ks, t): row 16*ks + 8*(g16/2) + 4*t + L16/4, bytes
-  // 512*dh + 64*md + 32*(g16&1) + 8*(L16&3); md = 2a + pm -> tr_base[ks][t][pm] + 128 a
+  for (int r = 0; r < 4; ++r) s_base[r] = kappa * kZRowB + zchunk(kappa, hf + 2 * r) * 16;
+  // transposed reads for key step ks, half t: row 16 ks + 8 (g16 / 2) + 4 t +
+  // L16 / 4, bytes 64 md + 32 (g16 & 1) + 8 (L16 & 3); md = 2c + pm ->
+  // tr_base[ks][t][pm] + 128 c
   const int g16 = lane >> 4, L16 = lane & 15;
   int tr_base[2][2][2];
 #pragma unroll
@@ -208,19 +226,27 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int pm = 0; pm < 2; ++pm) {
         const int row = 16 * ks + 8 * (g16 >> 1) + 4 * t + (L16 >> 2);
-        const int chunk = 32 * dh + 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
+        const int chunk = 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
         tr_base[ks][t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
       }
-  // the DMA loads of this wave: j = wave + 4 i (i < 9) fills LDS chunks
-  // 64 j + lane; keep (tile row << 8 | source chunk) per load, two per register
-  int dma_rc[(kDmaPerWave + 1) / 2];
+  // direct loads: load j of this wave fills LDS chunks 64 (wave + 4 j) + lane,
+  // i.e. tile row rr, source chunk cc (the XOR is its own inverse); its byte
+  // offset in a contiguous tile is rr * 1152 + cc * 16
+  // (offsets below 36 KB: two per register)
+  uint32_t dma_pk[(kDmaPerWave + 1) / 2];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int pch = (wave + kDecWaves * i) * 64 + lane;
-    const int row = pch / kZRowChunks;
-    const int rc = (row << 8) | zchunk(row, pch - row * kZRowChunks);  // XOR is its own inverse
-    if (i & 1) dma_rc[i >> 1] |= rc << 16; else dma_rc[i >> 1] = rc;
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int pch = (wave + kDecWaves * j) * 64 + lane;
+    const int rr = pch / kZRowChunks;
+    const uint32_t off = (uint32_t)(rr * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16);
+    if (j & 1) dma_pk[j >> 1] |= off << 16; else dma_pk[j >> 1] = off;
   }
+  auto dma_off = [&](int j) __attribute__((always_inline)) {
+    return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  };
+  const bool contiguous = (a.ps % kDecBN) == 0;
+  // LDS score steps: B operand = head row of the query table, chunk 2 r + hf
+  const int q_base = head * kQRowB + hf * 16;
 
   // first sequence touched: largest b with cum[b] <= s_lo
   int b;
@@ -238,10 +264,10 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     if (seg_end <= pos) { ++b; continue; }
     const int k0 = (int)(pos - a.cum[b]);
     const int k1 = (int)(seg_end - a.cum[b]);
-    const int ntiles = (k1 - k0 + kDecBN - 1) / kDecBN;
-    // the segment's page-table entries, staged in LDS once: the DMA queue then
-    // holds only tile loads, so waits on it never stall for a table lookup
-    const int lp0 = k0 / a.ps;
+    const int kt0 = k0 & ~(kDecBN - 1);
+    const int ntiles = (k1 - kt0 + kDecBN - 1) / kDecBN;
+    // the segment's page-table entries, staged in LDS once
+    const int lp0 = kt0 / a.ps;
     const int npg = (k1 - 1) / a.ps - lp0 + 1;
     __syncthreads();  // the previous segment is done with the page window and the stages
     for (int i = tid; i < min(npg, kPTWindow); i += kDecThreads) {
@@ -251,96 +277,131 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     }
     __syncthreads();
 
-    auto issue = [&](int tile, int stage) {
-      uint8_t* base = sZ + stage * kZStageB;
-      const int kt = k0 + tile * kDecBN;
-      // pool row of tile row (lane & 31); rows past the segment read a valid row
-      const int key = min(kt + (lane & 31), k1 - 1);
-      const int lp = key / a.ps;
-      const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+    // loads of tile t (keys kt0 + 32 t ..) into stage st
+    const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+      const uint32_t base = lds0 + st * kZStageB;
+      const int kt = kt0 + t * kDecBN;
+      // one contiguous piece when the page holds the whole tile and every row
+      // of it is a context row (rows past the context are never read)
+      if (contiguous && kt + kDecBN <= ctx_b) {
+        const int lp = kt / a.ps;
+        const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
+        const void* sb = uniform_ptr_d(cache + slot * kZRowB);
 #pragma unroll
-      for (int i = 0; i < kDmaPerWave; ++i) {
-        const int rc = (dma_rc[i >> 1] >> (16 * (i & 1))) & 0xFFFF;
-        const int rs = __shfl(slot, rc >> 8, 64);
-        dma16(cache + ((size_t)rs * kCache + (rc & 255) * 8), base + (wave + kDecWaves * i) * 1024);
+        for (int j = 0; j < kDmaPerWave; ++j)
+          dma16_s(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+      } else {
+        // pool slot of tile row (lane & 31); rows past the segment read its last
+        // row (a context row whose page is inside the staged window)
+        const int key = min(kt + (lane & 31), k1 - 1);
+        const int lp = key / a.ps;
+        const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+        int rs[kDmaPerWave];
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+          const int rr = ((wave + kDecWaves * j) * 64 + lane) / kZRowChunks;
+          rs[j] = __shfl(slot, rr, 64);
+        }
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+          const int rr = ((wave + kDecWaves * j) * 64 + lane) / kZRowChunks;
+          dma16(cache + (size_t)rs[j] * kZRowB + (dma_off(j) - rr * kZRowB),
+                base + (wave + kDecWaves * j) * 1024);
+        }
       }
     };
 
-    // absorbed queries of this wave's heads and depth half: 18 steps of 16
-    bf16x8 qf[18];
+    // absorbed queries of this wave's heads: score steps 0 .. 17 in
+    // registers, 18 .. 35 in the LDS table (row = head)
+    bf16x8 qf[kQRegSteps];
     {
-      const uint16_t* qp =
-          a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache + 288 * dh + hf * 8;
+      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache;
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        u32x4 v = hvalid ? *(const u32x4*)(qp + ks * 16) : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < kQRegSteps; ++ks) {
+        u32x4 v = hvalid ? *(const u32x4*)(qrow + ks * 16 + hf * 8) : u32x4{0, 0, 0, 0};
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
+      // table row of this lane's head: 36 chunks, this lane copies chunks hf, hf + 2, ..
+#pragma unroll
+      for (int r = 0; r < kQLdsSteps; ++r) {
+        const int ch = 2 * r + hf;
+        u32x4 v = hvalid ? *(const u32x4*)(qrow + kQRegSteps * 16 + ch * 8) : u32x4{0, 0, 0, 0};
+        *(u32x4*)(sQ + head * kQRowB + ch * 16) = v;
+      }
     }
+    __syncthreads();  // the query table is written
     // wait for q here, before any tile load is in flight: the compiler cannot
     // count the tile loads, so a wait it placed for q inside the tile loop
     // would drain them every tile (gfx9 encoding: vmcnt 0, others unlimited)
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    float m_ref = -INFINITY;   // reference maximum (log2 domain)
-    float m_seen = -INFINITY;  // largest scaled score of the segment (exact at the end)
-    f32x16 o[8];
+    f32x16 o[16];
 #pragma unroll
-    for (int md = 0; md < 8; ++md)
+    for (int md = 0; md < 16; ++md)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
+    float m_ref = -INFINITY;   // reference maximum (log2 domain): the first tile's
+    float m_seen = -INFINITY;  // largest scaled score of the segment
     float l_run = 0.f;
-    bool halted = false;  // wave-uniform: the partial is marked for recomputation
+    bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
-    issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
+#pragma unroll
+    for (int t = 0; t < kZStages - 1; ++t)
+      if (t < ntiles) issue(t, t);
 
     for (int t = 0; t < ntiles; ++t) {
-      // wait for this wave's loads of tile t (tile t+1's may stay in flight)
-      if (t + 1 < ntiles) {
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // = kDmaPerWave
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();
-      if (t + 2 < ntiles) issue(t + 2, (t + 2) % kZStages);
+      // wait for this wave's loads of tile t (the only ones in flight)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      static_assert(kZStages == 2, "one tile in flight");
+      __syncthreads();  // tile t landed for every wave; the stage of tile t-1 is free
+      if (t + kZStages - 1 < ntiles) issue(t + kZStages - 1, (t + kZStages - 1) % kZStages);
       const uint8_t* Z = sZ + (t % kZStages) * kZStageB;
-      const int kt = k0 + t * kDecBN;
+      const int kt = kt0 + t * kDecBN;
 
-      // partial scores over this wave's depth half, in two independent chains
+      // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
       f32x16 s, s2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { s[i] = 0.f; s2[i] = 0.f; }
 #pragma unroll
-      for (int ks = 0; ks < 18; ks += 2) {
+      for (int ks = 0; ks < 36; ks += 2) {
         const bf16x8 za = *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
         const bf16x8 zb = *(const bf16x8*)(Z + s_base[(ks + 1) & 3] + 128 * ((ks + 1) >> 2));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qf[ks], s, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, qf[ks + 1], s2, 0, 0, 0);
+        const bf16x8 qa = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0]
+                                          : *(const bf16x8*)(sQ + q_base + 32 * (ks - kQRegSteps));
+        const bf16x8 qb = ks + 1 < kQRegSteps
+                              ? qf[ks + 1 < kQRegSteps ? ks + 1 : 0]
+                              : *(const bf16x8*)(sQ + q_base + 32 * (ks + 1 - kQRegSteps));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qa, s, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, qb, s2, 0, 0, 0);
+      }
+      // LDS operands run about four MFMAs ahead: step i needs the key
+      // fragment (and from step 18 on the query fragment too)
+      __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 36; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+        if (i < 14) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+        else if (i < 32) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] += s2[i];
-      float* xw = sX + wave * 1024;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xw[i * 64 + lane] = s[i];
-      __syncthreads();
-      const float* xp = sX + (wave ^ 2) * 1024;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] += xp[i * 64 + lane];
 
       // register i holds tile row 16*(i/8) + 8*hf + i%8
-      if (kt + kDecBN > k1) {
+      if (kt < k0 || kt + kDecBN > k1) {
+        const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kt + (i >> 3) * 16 + hf * 8 + (i & 7) >= k1) s[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int c = (i >> 3) * 16 + (i & 7);
+          if (c < lo || c >= hi) s[i] = -INFINITY;
+        }
       }
       float tmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-      tmax = max_with_lane32(tmax);
-      const float mt = tmax * sl2;  // finite: every tile holds a valid row
+      const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
       m_seen = fmaxf(m_seen, mt);
-      if (m_ref == -INFINITY) m_ref = mt;
-      halted = halted || (__ballot(mt > m_ref + 64.0f) != 0);
+      if (t == 0) m_ref = mt;
+      halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
       const float neg_m = -m_ref;
       float psum = 0.f;
       bf16x8 pb[2];
@@ -356,12 +417,11 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         }
         pb[ks] = __builtin_bit_cast(bf16x8, wv);
       }
-      psum = sum_with_lane32(psum);
-      l_run += psum;
+      l_run += sum_with_lane32(psum);
 
-      // O^T[256 dims x 32 heads] += Z^T P^T, Z^T read transposed from the row tile
+      // ---- O^T[512 dims x 32 heads] += Z^T P^T ----
 #pragma unroll
-      for (int md = 0; md < 8; ++md)
+      for (int md = 0; md < 16; ++md)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x4 a0 = ds_read_tr16(Z + tr_base[ks][0][md & 1] + 128 * (md >> 1));
@@ -369,15 +429,22 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
           const bf16x8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
           o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
         }
+      // transposed reads eight ahead (four MFMAs) of the value product
+      __builtin_amdgcn_sched_group_barrier(0x0100, 8, 1);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);
+        if (i < 28) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
+      }
     }
 
     // partial state of (w, b): slot w + b
     if (hvalid) {
       const size_t base = ((size_t)(w + b) * a.H + head);
-      float* op = a.part_o + base * kLora + 256 * dh;
-      // O^T register i of block md: dim 32*md + 8*(i/4) + 4*hf + i%4 (within the half)
+      float* op = a.part_o + base * kLora;
+      // O^T register i of block md: dim 32*md + 8*(i/4) + 4*hf + i%4
 #pragma unroll
-      for (int md = 0; md < 8; ++md)
+      for (int md = 0; md < 16; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
@@ -385,10 +452,9 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
           for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
           *(f32x4*)(op + md * 32 + g * 8 + hf * 4) = v;
         }
-      if (hf == 0 && dh == 0) {
-        // an overflowing head group hands (exact maximum, -1) to the combine
-        // step, which recomputes this partial against that maximum
-        // (both waves of a head group hold the same summed scores and flags)
+      if (hf == 0) {
+        // a wave whose scores outgrew the reference hands (exact maximum, -1)
+        // to the combine step, which recomputes this partial against it
         a.part_ml[base * 2 + 0] = halted ? m_seen : m_ref;
         a.part_ml[base * 2 + 1] = halted ? -1.0f : l_run;
       }
@@ -402,7 +468,8 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 // prefix sums of the context lengths (one workgroup)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const uint32_t* ctx,
-                                                            int B) {
+                                                            int B, uint32_t* wstart, int2* wspan,
+                                                            int G) {
   __shared__ uint32_t s_scan[256];
   __shared__ uint32_t s_carry;
   const int tid = threadIdx.x;
@@ -425,28 +492,50 @@ __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const
     __syncthreads();
   }
   if (tid == 0) cum[0] = 0;
+  // key range w covers keys [wstart[w], wstart[w+1])
+  const uint32_t N = s_carry;
+  for (int w = tid; w <= G; w += 256) wstart[w] = (uint32_t)(((uint64_t)w * N) / G);
+  __threadfence();  // other threads of the workgroup read these entries below
+  __syncthreads();
+  // ranges holding sequence b's first and last keys (empty sequences: (0, -1))
+  for (int b = tid; b < B; b += 256) {
+    const uint32_t lo_key = cum[b], hi_key = cum[b + 1];
+    if (hi_key <= lo_key) { wspan[b] = make_int2(0, -1); continue; }
+    int lo = 0, hi = G - 1;  // largest w with wstart[w] <= lo_key
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wstart[mid] <= lo_key) lo = mid; else hi = mid - 1;
+    }
+    const int w_lo = lo;
+    hi = G - 1;              // largest w with wstart[w] < hi_key
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wstart[mid] < hi_key) lo = mid; else hi = mid - 1;
+    }
+    wspan[b] = make_int2(w_lo, lo);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 3. combine partial states: o_lat[b, h, :] (bf16)
+// 3. combine the partial states: o_lat[b, h, :] (bf16 hi + lo)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t split_start(int w, uint32_t N, int G) {
-  return (uint32_t)(((uint64_t)w * N) / G);
-}
+// One wave per (sequence, head), lane l owns dims 8 l .. 8 l + 7: the maximum
+// over the partials first, then their weighted sum. Thousands of independent
+// waves keep many loads in flight. o_lat is written as a bf16 pair (hi, lo)
+// so that the projection, on bf16 MFMA, sees it unrounded to 8 bits.
+constexpr int kCmbHeads = 4;  // heads (waves) per workgroup
 
-// Recompute the partial of (range w, sequence b, head h) against the exact
-// maximum m (log2 domain) the split kernel recorded. Plain fp32 arithmetic,
-// one key per thread for the scores; only reached for extreme score ranges.
+// Recompute, in one wave, the partial of (range w, sequence b, head h) against
+// the exact maximum m (log2 domain) the split kernel recorded: plain fp32,
+// one key per lane for the scores. Returns the lane's 8 dims and the sum.
+// Only reached for extreme score ranges.
 __device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, float m,
-                                  float* sh_q, float* sh_p) {
-  const int tid = threadIdx.x;
-  const uint32_t N = c.cum[c.B];
-  const uint32_t lo = max(split_start(w, N, c.G), c.cum[b]);
-  const uint32_t hi = min(split_start(w + 1, N, c.G), c.cum[b + 1]);
+                                  float (&acc)[8], float& lsum) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = max(c.wstart[w], c.cum[b]);
+  const uint32_t hi = min(c.wstart[w + 1], c.cum[b + 1]);
   const int k0 = (int)(lo - c.cum[b]), k1 = (int)(hi - c.cum[b]);
   const uint16_t* qa = c.q_abs + ((size_t)b * c.H + h) * kCache;
-  for (int e = tid; e < kCache; e += 256) sh_q[e] = bf16_to_f32(qa[e]);
-  __syncthreads();
   const uint16_t* cache = (const uint16_t*)c.cache;
   auto row_of = [&](int key) -> const uint16_t* {
     const int lp = key / c.ps;
@@ -454,94 +543,77 @@ __device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, flo
     if (pg < 0 || pg >= c.num_pages) pg = 0;
     return cache + ((size_t)pg * c.ps + (key - lp * c.ps)) * kCache;
   };
-  float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
-  const int d = 2 * tid;
-  for (int kc = k0; kc < k1; kc += 256) {
-    const int key = kc + tid;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  lsum = 0.f;
+  for (int kc = k0; kc < k1; kc += 64) {
+    const int key = kc + lane;
     float p = 0.f;
     if (key < k1) {
       const uint16_t* z = row_of(key);
       float sc = 0.f;
-      for (int e = 0; e < kCache; ++e) sc = fmaf(sh_q[e], bf16_to_f32(z[e]), sc);
+      for (int e = 0; e < kCache; ++e) sc = fmaf(bf16_to_f32(qa[e]), bf16_to_f32(z[e]), sc);
       p = __builtin_amdgcn_exp2f(sc * c.scale_log2 - m);
     }
-    sh_p[tid] = p;
-    __syncthreads();
-    const int n = min(256, k1 - kc);
+    const int n = min(64, k1 - kc);
     for (int k = 0; k < n; ++k) {
-      const float pk = sh_p[k];
-      const uint16_t* z = row_of(kc + k);
-      acc0 = fmaf(pk, bf16_to_f32(z[d]), acc0);
-      acc1 = fmaf(pk, bf16_to_f32(z[d + 1]), acc1);
+      const float pk = __shfl(p, k, 64);
+      const uint16_t* z = row_of(kc + k) + 8 * lane;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(pk, bf16_to_f32(z[j]), acc[j]);
       lsum += pk;
     }
-    __syncthreads();
   }
-  const size_t base = (size_t)(w + b) * c.H + h;
-  c.part_o[base * kLora + d] = acc0;
-  c.part_o[base * kLora + d + 1] = acc1;
-  __syncthreads();
-  if (tid == 0) {
-    c.part_ml[base * 2 + 0] = m;
-    c.part_ml[base * 2 + 1] = lsum;
-  }
-  __syncthreads();
 }
 
-__global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
-  __shared__ float sh_q[kCache];
-  __shared__ float sh_p[256];
-  // one workgroup per (b, h); 256 threads x 2 dims
-  const int bh = blockIdx.x;
-  const int b = bh / c.H;
-  const int h = bh - b * c.H;
-  const uint32_t N = c.cum[c.B];
-  const uint32_t lo_key = c.cum[b], hi_key = c.cum[b + 1];  // keys [lo_key, hi_key)
-  if (hi_key <= lo_key) return;
-  // ranges touching the sequence: w_lo holds lo_key, w_hi holds hi_key - 1
-  int w_lo, w_hi;
-  {
-    int lo = 0, hi = c.G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (split_start(mid, N, c.G) <= lo_key) lo = mid; else hi = mid - 1;
+__global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineArgs c) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y * kCmbHeads + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= c.H) return;
+  const int2 span = c.wspan[b];
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  if (span.y >= span.x) {
+    float M = -INFINITY;
+    for (int w = span.x; w <= span.y; ++w) {
+      if (c.wstart[w] >= c.wstart[w + 1]) continue;  // empty range: no partial
+      M = fmaxf(M, c.part_ml[((size_t)(w + b) * c.H + h) * 2]);
     }
-    w_lo = lo;
-    lo = w_lo; hi = c.G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (split_start(mid, N, c.G) < hi_key) lo = mid; else hi = mid - 1;
+    float L = 0.f;
+    for (int w = span.x; w <= span.y; ++w) {
+      if (c.wstart[w] >= c.wstart[w + 1]) continue;
+      const size_t base = (size_t)(w + b) * c.H + h;
+      const float m = c.part_ml[base * 2];
+      float l = c.part_ml[base * 2 + 1];
+      float ow[8];
+      if (l < 0.f) {  // marked partial: recompute (wave-uniform)
+        recompute_partial(c, w, b, h, m, ow, l);
+      } else {
+        const f32x4 v0 = *(const f32x4*)(c.part_o + base * kLora + 8 * lane);
+        const f32x4 v1 = *(const f32x4*)(c.part_o + base * kLora + 8 * lane + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { ow[j] = v0[j]; ow[4 + j] = v1[j]; }
+      }
+      const float wt = __builtin_amdgcn_exp2f(m - M);
+      L += wt * l;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wt, ow[j], acc[j]);
     }
-    w_hi = lo;
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv;
   }
-  float M = -INFINITY;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    if (split_start(w, N, c.G) >= split_start(w + 1, N, c.G)) continue;  // empty range
-    const size_t base = (size_t)(w + b) * c.H + h;
-    const float m = c.part_ml[base * 2];
-    if (c.part_ml[base * 2 + 1] < 0.f) recompute_partial(c, w, b, h, m, sh_q, sh_p);
-    M = fmaxf(M, m);
+  u32x4 hi, lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hi[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+    lo[j] = pack_bf16x2(acc[2 * j] - bf16_lo(hi[j]), acc[2 * j + 1] - bf16_hi(hi[j]));
   }
-  float lsum = 0.f, acc0 = 0.f, acc1 = 0.f;
-  const int d = threadIdx.x * 2;
-  for (int w = w_lo; w <= w_hi; ++w) {
-    if (split_start(w, N, c.G) >= split_start(w + 1, N, c.G)) continue;
-    const size_t base = (size_t)(w + b) * c.H + h;
-    const float wt = __builtin_amdgcn_exp2f(c.part_ml[base * 2] - M);
-    lsum += wt * c.part_ml[base * 2 + 1];
-    const float2 v = *(const float2*)(c.part_o + base * kLora + d);
-    acc0 += wt * v.x;
-    acc1 += wt * v.y;
-  }
-  const float inv = 1.f / lsum;
-  // o_lat as a bf16 pair (hi + lo): the output projection runs on bf16 MFMA
-  // and takes both terms, so o_lat is not rounded to 8 bits on the way
-  const float v0 = acc0 * inv, v1 = acc1 * inv;
-  const uint32_t hi = pack_bf16x2(v0, v1);
-  const uint32_t lo = pack_bf16x2(v0 - bf16_lo(hi), v1 - bf16_hi(hi));
   uint16_t* orow = c.o_lat + ((size_t)b * c.H + h) * (2 * kLora);
-  *(uint32_t*)(orow + d) = hi;
-  *(uint32_t*)(orow + kLora + d) = lo;
+  *(u32x4*)(orow + 8 * lane) = hi;
+  *(u32x4*)(orow + kLora + 8 * lane) = lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -572,19 +644,21 @@ hipError_t launch_decode_absorb(void* q_abs, const uint16_t* q, const uint16_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, B);
+hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, uint32_t* wstart,
+                                int2* wspan, int G, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, B, wstart,
+                     wspan, G);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
-  const int grid = a.halves == 2 ? 16 * ((a.G + 7) / 8) : a.G;
-  hipLaunchKernelGGL(decode_split_kernel, dim3(grid), dim3(kDecThreads), 0, stream, a);
+  hipLaunchKernelGGL(decode_split_kernel, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const CombineArgs& c, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(c.B * c.H), dim3(256), 0, stream, c);
+  const dim3 grid(c.B, (c.H + kCmbHeads - 1) / kCmbHeads);
+  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64 * kCmbHeads), 0, stream, c);
   return hipGetLastError();
 }
 

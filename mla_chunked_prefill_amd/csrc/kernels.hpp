@@ -48,17 +48,21 @@ struct DecodeArgs {
   const void* cache;         // [num_pages][ps][576]
   const int32_t* page_table; // [B][maxp]
   const uint32_t* cum;       // [B+1] prefix sums of the context lengths
+  const uint32_t* wstart;    // [G+1] first key of every key range
   float* part_o;             // [G + B][H][512]
   float* part_ml;            // [G + B][H][2]
-  int B, H, ps, maxp, num_pages, G, halves;
+  int B, H, ps, maxp, num_pages, G;
   float scale_log2;
 };
 struct CombineArgs {
   uint16_t* o_lat;           // [B][H][2][512] bf16: hi then lo
   float* part_o;             // [G + B][H][512]
-  float* part_ml;            // [G + B][H][2]; a negative sum marks a partial to recompute
+  float* part_ml;            // [G + B][H][2] (max in the log2 domain, sum; a
+                             // negative sum marks a partial to recompute)
   const uint32_t* cum;       // [B+1]
-  const uint16_t* q_abs;     // [B][H][576]
+  const uint32_t* wstart;    // [G+1]
+  const int2* wspan;         // [B]: first and last key range touching each sequence
+  const uint16_t* q_abs;     // [B][H][576], for recomputation
   const void* cache;
   const int32_t* page_table;
   int B, H, G, ps, maxp, num_pages;
@@ -74,7 +78,8 @@ hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
 hipError_t launch_decode_absorb(void*, const uint16_t*, const uint16_t*, int, int, bool,
                                 hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, hipStream_t);
-hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, hipStream_t);
+hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, uint32_t*, int2*, int,
+                                hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);
