@@ -10,7 +10,8 @@ the timed region. HIP events recorded on that stream around every call give
 per-call durations; the attention call is the dominant kernel.
 
 A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
-batch (contexts U{4096..32768}) and reports achieved HBM bandwidth.
+batch (contexts U{4096..32768}), with a bf16 and then an e4m3 cache, and
+reports achieved HBM bandwidth.
 
 One JSON line is printed. "value" is the end-to-end prefill rate in
 algorithmic attention TFLOP/s (attention FLOPs / whole step time);
@@ -141,17 +142,18 @@ def bench_prefill(args, binding, torch):
         attn_flop=attn_flop, gemm_flop=gemm_flop, pairs=pairs, max_rows=max_rows)
 
 
-def bench_decode(args, binding, torch):
+def bench_decode(args, binding, torch, recipe="decode_b64"):
     from workloads import decode_recipe
     from workloads.device import decode_tensors
 
-    wl = decode_recipe("decode_b64")
+    wl = decode_recipe(recipe)
     t = decode_tensors(wl)
     B, H = wl.batch, wl.num_heads
     max_ctx = int(wl.context_lens.max())
+    code = binding.MLA_FP8_E4M3FN if wl.fp8 else binding.MLA_BF16
     out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, wl.page_size, 0, 0), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, wl.page_size, 0, code),
+                     dtype=torch.uint8, device="cuda")
 
     def call():
         binding.mla_decode(out, t["q"], t["context_lengths"], t["kv_cache"], t["page_table"],
@@ -171,7 +173,8 @@ def bench_decode(args, binding, torch):
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
     ctx_rows = int(wl.context_lens.astype("int64").sum())
-    bytes_alg = (ctx_rows * 576 * 2 + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2)
+    row_bytes = 576 * (1 if wl.fp8 else 2)
+    bytes_alg = (ctx_rows * row_bytes + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2)
     flop = 2 * (576 + 512) * H * ctx_rows
     return dict(ms=ms, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows)
 
@@ -283,6 +286,17 @@ def main():
             "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes": dd["bytes"],
             "tflops": round(dd["flop"] / (dd["ms"] * 1e-3) / 1e12, 2),
+        }
+        d8 = bench_decode(args, binding, torch, "decode_b64_fp8")
+        gbps = d8["bytes"] / (d8["ms"] * 1e-3) / 1e9
+        line["decode_fp8"] = {
+            "workload": "decode_b64_fp8: as decode_b64 with the cache stored float8_e4m3fn "
+                        "(unit amax)",
+            "ms": round(d8["ms"], 4),
+            "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": d8["bytes"],
+            "tflops": round(d8["flop"] / (d8["ms"] * 1e-3) / 1e12, 2),
         }
     if not args.no_cpu:
         tf, sec, threads = cpu_baseline(p["wl"], args.cpu_heads)

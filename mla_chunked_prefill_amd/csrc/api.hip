@@ -109,12 +109,12 @@ int decode_groups(int B, int max_ctx, int page_size, int num_partitions) {
   return g;
 }
 
-// decode workspace: q_abs [B][H][576], cum [B+1] u32, wstart [G+1] u32,
+// decode workspace: q_abs [B][H][576] bf16, cum [B+1] u32, wstart [G+1] u32,
 // wspan [B] int2, part_o [G+B][H][512] f32, part_ml [G+B][H][2] f32, o_lat
 // [B][H][2][512] bf16 (hi, lo). G split workgroups cover the batch's
 // concatenated contexts in equal ranges.
 struct DecodeWs {
-  void* q_abs;
+  uint16_t* q_abs;
   uint32_t* cum;
   uint32_t* wstart;
   int2* wspan;
@@ -130,8 +130,8 @@ DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
   w.G = decode_groups(B, max_ctx, page_size, num_partitions);
   const size_t slots = (size_t)w.G + B;
   size_t off = 0;
-  w.q_abs = base + off;
-  off = align_up(off + (size_t)B * H * mla::kCache * dsize(cache_dtype));
+  w.q_abs = (uint16_t*)(base + off);
+  off = align_up(off + (size_t)B * H * mla::kCache * 2);
   w.cum = (uint32_t*)(base + off);
   off = align_up(off + (size_t)(B + 1) * sizeof(uint32_t));
   w.wstart = (uint32_t*)(base + off);
@@ -386,8 +386,6 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   if (!output || !q || !context_lengths || !kv_cache || !page_table || !w_uk || !w_uv)
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer");
   if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_decode: dtype");
-  if (cache_dtype == MLA_FP8_E4M3FN)
-    return fail(MLA_ERR_UNSUPPORTED, "mla_decode: e4m3 cache not built yet");
   if (batch_size < 1 || num_heads < 1 || num_heads > 128 || page_size < 1 ||
       max_pages_per_seq < 1 || num_pages < 1 || max_context_len < 1 || num_partitions < 0 ||
       num_partitions > 65536 || !(scale > 0.f))
@@ -405,7 +403,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   const bool fp8 = cache_dtype == MLA_FP8_E4M3FN;
   int st = hip_status(mla::launch_decode_absorb(ws.q_abs, (const uint16_t*)q,
                                                 (const uint16_t*)w_uk, batch_size, num_heads,
-                                                fp8, stream),
+                                                stream),
                       "absorb kernel");
   if (st != MLA_OK) return st;
   st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, ws.wstart,
@@ -427,7 +425,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   a.num_pages = num_pages;
   a.G = ws.G;
   a.scale_log2 = scale * kLog2e;
-  st = hip_status(mla::launch_decode_split(a, stream), "split-KV kernel");
+  st = hip_status(mla::launch_decode_split(a, fp8, stream), "split-KV kernel");
   if (st != MLA_OK) return st;
   mla::CombineArgs c;
   c.o_lat = ws.o_lat;
@@ -446,6 +444,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   c.maxp = max_pages_per_seq;
   c.num_pages = num_pages;
   c.scale_log2 = scale * kLog2e;
+  c.fp8 = fp8;
   st = hip_status(mla::launch_decode_combine(c, stream), "combine kernel");
   if (st != MLA_OK) return st;
   return hip_status(mla::launch_decode_project((uint16_t*)output, ws.o_lat,

@@ -18,17 +18,16 @@
 
 namespace mla {
 
-typedef long fp8x8_d;
-
 // ---------------------------------------------------------------------------
 // 1, 4. per-head small GEMMs: C[b, n] = sum_k X[b, k] W[n, k]
 // ---------------------------------------------------------------------------
 // X rows: x + b*x_stride (K contiguous, bf16); W rows: w + n*K (K contiguous).
-// Output: y[b*y_stride + n] as bf16 (or e4m3 when kFp8Out). One wave computes a
-// 32 (b) x 32 (n) tile; K is a multiple of 16.
-template <int K, bool kFp8Out, bool kTwoTerm = false>
+// Output: y[b*y_stride + n] as bf16. One wave computes a 32 (b) x 32 (n) tile;
+// K is a multiple of 16. kTwoTerm: X = hi + lo, with lo stored K elements
+// after hi.
+template <int K, bool kTwoTerm = false>
 __global__ void __launch_bounds__(256) head_gemm_kernel(
-    void* __restrict__ y, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ y, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     int B, int N, long x_stride_b, long x_stride_h, long w_stride_h, long y_stride_b,
     long y_stride_h, int n_tiles_n) {
   const int wave = threadIdx.x >> 6;
@@ -55,7 +54,7 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
     const u32x4 wb = *(const u32x4*)(wp + k0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xa),
                                                   __builtin_bit_cast(bf16x8, wb), acc, 0, 0, 0);
-    if (kTwoTerm) {  // x = hi + lo, lo stored K elements after hi
+    if (kTwoTerm) {
       u32x4 xl = *(const u32x4*)(xp + K + k0);
       if (brow >= B) xl = u32x4{0, 0, 0, 0};
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xl),
@@ -68,23 +67,19 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
     const int bb = tb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
     if (bb < B) {
       const long o = (long)bb * y_stride_b + (long)h * y_stride_h + nrow;
-      if (kFp8Out) ((uint8_t*)y)[o] = (uint8_t)f32_to_e4m3_sat(acc[i]);
-      else ((uint16_t*)y)[o] = (uint16_t)f32_to_bf16_rne(acc[i]);
+      y[o] = (uint16_t)f32_to_bf16_rne(acc[i]);
     }
   }
 }
 
-// copy q_rope into the last 64 columns of q_abs (bf16, or e4m3 for an fp8 cache)
-template <bool kFp8Out>
-__global__ void copy_rope_kernel(void* __restrict__ q_abs, const uint16_t* __restrict__ q,
+// copy q_rope into the last 64 columns of q_abs
+__global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q,
                                  int B, int H) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*H*64
   if (i >= (long)B * H * kRope) return;
   const long bh = i / kRope;
   const int e = (int)(i - bh * kRope);
-  const uint16_t v = q[bh * kQDepth + kNope + e];
-  if (kFp8Out) ((uint8_t*)q_abs)[bh * kCache + kLora + e] = (uint8_t)f32_to_e4m3_sat(bf16_to_f32(v));
-  else ((uint16_t*)q_abs)[bh * kCache + kLora + e] = v;
+  q_abs[bh * kCache + kLora + e] = q[bh * kQDepth + kNope + e];
 }
 
 // ---------------------------------------------------------------------------
@@ -145,6 +140,15 @@ constexpr int kQRowB = kQLdsSteps * 32 + 16;        // 592 bytes
 constexpr int kQTabB = 128 * kQRowB;
 constexpr float kDecSlack = 64.0f;
 static_assert(kZLoads % kDecWaves == 0, "every wave issues the same loads");
+// e4m3 cache: a tile (32 rows of 576 bytes, rows kept as stored) is loaded
+// into one of two staging buffers behind the single bf16 stage, and widened
+// exactly into the bf16 stage (8 codes per thread and step) before use
+constexpr int kF8RowB = kCache;                     // 576 bytes
+constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
+constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
+constexpr int kF8Units = kDecBN * kZRowChunks;      // 2304 groups of 8 codes per tile
+static_assert(kZStageB + 2 * kF8StageB <= kZStages * kZStageB, "staging fits the stages");
+static_assert(kF8Units % kDecThreads == 0, "every thread widens the same number of groups");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
 __device__ __forceinline__ int zswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
@@ -185,6 +189,18 @@ __device__ __forceinline__ const void* uniform_ptr_d(const void* p) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
+// 8 e4m3fn codes -> 8 bf16 values (exact: every e4m3fn value, subnormals
+// included, is a bf16 normal number or zero)
+__device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
+  return o;
+}
+
+template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
   // second half of the absorbed queries (B operand of the last 18 score steps)
@@ -280,8 +296,37 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     // loads of tile t (keys kt0 + 32 t ..) into stage st
     const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
     auto issue = [&](int t, int st) __attribute__((always_inline)) {
-      const uint32_t base = lds0 + st * kZStageB;
       const int kt = kt0 + t * kDecBN;
+      if constexpr (kFp8) {
+        // staging st holds the tile's rows as stored: load p (of 1152) of 16
+        // bytes covers bytes 16 p, i.e. row p / 36, bytes 16 (p % 36) of it
+        const uint32_t base = lds0 + kZStageB + st * kF8StageB;
+        if (contiguous && kt + kDecBN <= ctx_b) {
+          const int lp = kt / a.ps;
+          const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
+          const void* sb = uniform_ptr_d(cache + slot * kF8RowB);
+#pragma unroll
+          for (int j = 0; j < (kF8Loads + kDecWaves - 1) / kDecWaves; ++j)
+            if (wave + kDecWaves * j < kF8Loads)
+              dma16_s(sb, (uint32_t)((wave + kDecWaves * j) * 1024 + lane * 16),
+                      base + (wave + kDecWaves * j) * 1024);
+        } else {
+          const int key = min(kt + (lane & 31), k1 - 1);
+          const int lp = key / a.ps;
+          const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+#pragma unroll
+          for (int j = 0; j < (kF8Loads + kDecWaves - 1) / kDecWaves; ++j) {
+            const int p = (wave + kDecWaves * j) * 64 + lane;
+            const int rr = p / (kF8RowB / 16);
+            const int rs = __shfl(slot, rr, 64);
+            if (wave + kDecWaves * j < kF8Loads)
+              dma16(cache + (size_t)rs * kF8RowB + (p - rr * (kF8RowB / 16)) * 16,
+                    base + (wave + kDecWaves * j) * 1024);
+          }
+        }
+        return;
+      }
+      const uint32_t base = lds0 + st * kZStageB;
       // one contiguous piece when the page holds the whole tile and every row
       // of it is a context row (rows past the context are never read)
       if (contiguous && kt + kDecBN <= ctx_b) {
@@ -345,17 +390,28 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     float l_run = 0.f;
     bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
-#pragma unroll
-    for (int t = 0; t < kZStages - 1; ++t)
-      if (t < ntiles) issue(t, t);
+    issue(0, 0);  // ntiles >= 1
 
     for (int t = 0; t < ntiles; ++t) {
       // wait for this wave's loads of tile t (the only ones in flight)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       static_assert(kZStages == 2, "one tile in flight");
-      __syncthreads();  // tile t landed for every wave; the stage of tile t-1 is free
-      if (t + kZStages - 1 < ntiles) issue(t + kZStages - 1, (t + kZStages - 1) % kZStages);
-      const uint8_t* Z = sZ + (t % kZStages) * kZStageB;
+      // tile t landed for every wave; every wave is done with tile t-1 (its
+      // bf16 stage, and for e4m3 the staging buffer of tile t+1)
+      __syncthreads();
+      if (t + 1 < ntiles) issue(t + 1, (t + 1) % 2);
+      const uint8_t* Z = sZ + (kFp8 ? 0 : (t % 2) * kZStageB);
+      if constexpr (kFp8) {
+        const uint8_t* F = sZ + kZStageB + (t % 2) * kF8StageB;
+#pragma unroll
+        for (int i = 0; i < kF8Units / kDecThreads; ++i) {
+          const int u = tid + kDecThreads * i;  // row u / 72, bf16 chunk u % 72
+          const int r = u / kZRowChunks, c = u - r * kZRowChunks;
+          const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
+          *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
+        }
+        __syncthreads();  // the bf16 tile is complete
+      }
       const int kt = kt0 + t * kDecBN;
 
       // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
@@ -536,12 +592,15 @@ __device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, flo
   const uint32_t hi = min(c.wstart[w + 1], c.cum[b + 1]);
   const int k0 = (int)(lo - c.cum[b]), k1 = (int)(hi - c.cum[b]);
   const uint16_t* qa = c.q_abs + ((size_t)b * c.H + h) * kCache;
-  const uint16_t* cache = (const uint16_t*)c.cache;
-  auto row_of = [&](int key) -> const uint16_t* {
+  const size_t esz = c.fp8 ? 1 : 2;
+  auto row_of = [&](int key) -> const uint8_t* {
     const int lp = key / c.ps;
     int pg = lp < c.maxp ? c.page_table[(size_t)b * c.maxp + lp] : 0;
     if (pg < 0 || pg >= c.num_pages) pg = 0;
-    return cache + ((size_t)pg * c.ps + (key - lp * c.ps)) * kCache;
+    return (const uint8_t*)c.cache + ((size_t)pg * c.ps + (key - lp * c.ps)) * kCache * esz;
+  };
+  auto elem = [&](const uint8_t* z, int e) -> float {
+    return c.fp8 ? e4m3_to_f32(z[e]) : bf16_to_f32(((const uint16_t*)z)[e]);
   };
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
@@ -550,17 +609,17 @@ __device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, flo
     const int key = kc + lane;
     float p = 0.f;
     if (key < k1) {
-      const uint16_t* z = row_of(key);
+      const uint8_t* z = row_of(key);
       float sc = 0.f;
-      for (int e = 0; e < kCache; ++e) sc = fmaf(bf16_to_f32(qa[e]), bf16_to_f32(z[e]), sc);
+      for (int e = 0; e < kCache; ++e) sc = fmaf(bf16_to_f32(qa[e]), elem(z, e), sc);
       p = __builtin_amdgcn_exp2f(sc * c.scale_log2 - m);
     }
     const int n = min(64, k1 - kc);
     for (int k = 0; k < n; ++k) {
       const float pk = __shfl(p, k, 64);
-      const uint16_t* z = row_of(kc + k) + 8 * lane;
+      const uint8_t* z = row_of(kc + k);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(pk, bf16_to_f32(z[j]), acc[j]);
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(pk, elem(z, 8 * lane + j), acc[j]);
       lsum += pk;
     }
   }
@@ -619,28 +678,18 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_decode_absorb(void* q_abs, const uint16_t* q, const uint16_t* w_uk, int B,
-                                int H, bool fp8_out, hipStream_t stream) {
+hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16_t* w_uk, int B,
+                                int H, hipStream_t stream) {
   // q_lat[b, h, l] = sum_d q[b, h, d] w_uk[h, l, d]: X = q (stride 192 per h),
   // W = w_uk[h] rows (l), K = 128, N = 512
   const int ntn = kLora / 32;
   const int tiles = ((B + 31) / 32) * ntn;
   const dim3 grid((tiles + 3) / 4, H);
-  if (fp8_out)
-    hipLaunchKernelGGL((head_gemm_kernel<kNope, true>), grid, dim3(256), 0, stream, q_abs, q,
-                       w_uk, B, kLora, (long)H * kQDepth, (long)kQDepth, (long)kLora * kNope,
-                       (long)H * kCache, (long)kCache, ntn);
-  else
-    hipLaunchKernelGGL((head_gemm_kernel<kNope, false>), grid, dim3(256), 0, stream, q_abs, q,
-                       w_uk, B, kLora, (long)H * kQDepth, (long)kQDepth, (long)kLora * kNope,
-                       (long)H * kCache, (long)kCache, ntn);
+  hipLaunchKernelGGL((head_gemm_kernel<kNope>), grid, dim3(256), 0, stream, q_abs, q, w_uk,
+                     B, kLora, (long)H * kQDepth, (long)kQDepth, (long)kLora * kNope,
+                     (long)H * kCache, (long)kCache, ntn);
   const long n = (long)B * H * kRope;
-  if (fp8_out)
-    hipLaunchKernelGGL(copy_rope_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream,
-                       q_abs, q, B, H);
-  else
-    hipLaunchKernelGGL(copy_rope_kernel<false>, dim3((n + 255) / 256), dim3(256), 0, stream,
-                       q_abs, q, B, H);
+  hipLaunchKernelGGL(copy_rope_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, q_abs, q, B, H);
   return hipGetLastError();
 }
 
@@ -651,8 +700,11 @@ hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, uint3
   return hipGetLastError();
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_split_kernel, dim3(a.G), dim3(kDecThreads), 0, stream, a);
+hipError_t launch_decode_split(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(a.G), dim3(kDecThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -669,7 +721,7 @@ hipError_t launch_decode_project(uint16_t* out, const uint16_t* o_lat, const uin
   const int ntn = kV / 32;
   const int tiles = ((B + 31) / 32) * ntn;
   const dim3 grid((tiles + 3) / 4, H);
-  hipLaunchKernelGGL((head_gemm_kernel<kLora, false, true>), grid, dim3(256), 0, stream, out,
+  hipLaunchKernelGGL((head_gemm_kernel<kLora, true>), grid, dim3(256), 0, stream, out,
                      o_lat, w_uv, B, kV, (long)H * 2 * kLora, (long)2 * kLora,
                      (long)kV * kLora, (long)H * kV, (long)kV, ntn);
   return hipGetLastError();

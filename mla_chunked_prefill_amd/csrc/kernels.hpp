@@ -45,7 +45,7 @@ struct AttnArgs {
 };
 struct DecodeArgs {
   const uint16_t* q_abs;     // [B][H][576] bf16
-  const void* cache;         // [num_pages][ps][576]
+  const void* cache;         // [num_pages][ps][576] bf16 or e4m3fn
   const int32_t* page_table; // [B][maxp]
   const uint32_t* cum;       // [B+1] prefix sums of the context lengths
   const uint32_t* wstart;    // [G+1] first key of every key range
@@ -67,6 +67,7 @@ struct CombineArgs {
   const int32_t* page_table;
   int B, H, G, ps, maxp, num_pages;
   float scale_log2;
+  bool fp8;                  // cache holds e4m3fn codes (else bf16)
 };
 hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,
                        const uint32_t*, int, int, uint32_t, hipStream_t);
@@ -75,9 +76,9 @@ hipError_t launch_up_project(const GemmArgs&, bool, hipStream_t);
 int attn_num_slots(int B, int total_q);
 hipError_t launch_attn_schedule(int2*, const uint32_t*, int, int, hipStream_t);
 hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
-hipError_t launch_decode_absorb(void*, const uint16_t*, const uint16_t*, int, int, bool,
+hipError_t launch_decode_absorb(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                 hipStream_t);
-hipError_t launch_decode_split(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
 hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, uint32_t*, int2*, int,
                                 hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);

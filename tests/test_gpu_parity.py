@@ -15,7 +15,7 @@ import torch
 
 from oracle import oracle
 from workloads import (Dims, decode_recipe, make_decode, make_prefill, prefill_recipe,
-                       prefill_recipe_lengths, f32_to_bf16_bits)
+                       prefill_recipe_lengths, f32_to_bf16_bits, f32_to_e4m3fn_codes)
 from workloads.device import bf16_bits, decode_tensors, fp8_bits, prefill_tensors
 
 pytestmark = pytest.mark.gpu
@@ -329,21 +329,81 @@ def test_decode_b64_sampled(B):
     _assert_close(got[idx], ref, BF16_MAX, BF16_MEAN)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("parts", [0, 1])
-def test_decode_extreme_score_range_recomputed(B, parts):
+def test_decode_extreme_score_range_recomputed(B, parts, fp8):
     """One late cache row whose rope part is 16 * sign(q_rope) of head 0 (latent
     part zero): its logit for head 0 exceeds the other rows' by ~80 log2 units,
     more than the split kernel's 64-unit range, so with one key range (parts =
     1; the row sits in the 19th tile of its segment) that partial is handed to
     the combine step's recomputation; without it exp2 would overflow fp32. The
-    rope half of q enters the scores unrounded, so bf16 bounds apply as usual."""
-    wl = make_decode("ext", 61, [700, 300], 8, 16)
+    rope half of q enters the scores unrounded, so bf16 bounds apply as usual
+    (16 and 0 are exact in e4m3 too)."""
+    wl = make_decode("ext", 61, [700, 300], 8, 16, fp8=fp8)
     dec = oracle.DecodedDecode(wl)
     row = np.zeros(576, dtype=np.float32)
     row[512:] = 16.0 * np.sign(dec.q[0, 0, 128:])
     p = 600  # position in sequence 0, well after its first tiles
     slot = int(wl.page_table[0, p // wl.page_size]) * wl.page_size + p % wl.page_size
-    wl.pool.reshape(-1, 576)[slot] = f32_to_bf16_bits(row)
+    wl.pool.reshape(-1, 576)[slot] = f32_to_e4m3fn_codes(row) if fp8 else f32_to_bf16_bits(row)
     got = _run_decode(B, wl, parts)
     ref = oracle.decode(wl)
-    _assert_close(got, ref, BF16_MAX, BF16_MEAN)
+    if fp8:
+        _assert_close(got, ref, FP8_MAX)
+    else:
+        _assert_close(got, ref, BF16_MAX, BF16_MEAN)
+
+
+# decode over an e4m3fn cache: rows are widened exactly to bf16 and both
+# products run on bf16 MFMA, so only the bf16 roundings of the scores'
+# probabilities and of q_lat separate the result from the oracle
+
+
+@pytest.mark.parametrize("parts", [0, 3])
+def test_decode_fp8_small_full(B, parts):
+    wl = make_decode("d8", 53, [1, 37, 300, 64, 1000], 8, 16, fp8=True)
+    _assert_close(_run_decode(B, wl, parts), oracle.decode(wl), FP8_MAX)
+
+
+def test_decode_fp8_all_heads_full(B):
+    wl = make_decode("d8_128", 54, [5000, 129, 2], 128, 64, fp8=True)
+    _assert_close(_run_decode(B, wl), oracle.decode(wl), FP8_MAX)
+
+
+def test_decode_fp8_single_key_widening_exact(B):
+    """Contexts of one key: the softmax weight is exactly 1, so o_lat is the
+    stored latent row itself and the output is w_uv times that row, summed in
+    fp32 and rounded once to bf16. The rows are set to chosen e4m3fn codes:
+    sequences 0..31 hold only subnormal codes (exponent field 0), the others
+    every finite code at random, up to +-448. Each output element must be
+    within one bf16 rounding (2^-8 relative) plus the fp32 summation bound
+    (2^-20 of the sum of |w z|) of the exact value, so a code widened wrongly
+    (a subnormal flushed, a wrong exponent bias) fails."""
+    wl = make_decode("d8_one", 55, [1] * 64, 8, 16, fp8=True)
+    rng = np.random.default_rng(56)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    subn = np.array([c for c in range(256) if (c & 0x78) == 0], dtype=np.uint8)
+    rows = wl.pool.reshape(-1, 576)
+    for b in range(64):
+        slot = int(wl.page_table[b, 0]) * wl.page_size
+        rows[slot] = rng.choice(subn if b < 32 else finite, 576)
+    got = _run_decode(B, wl)
+    ref = oracle.decode(wl)
+    dec = oracle.DecodedDecode(wl)
+    for b in range(64):
+        z = np.abs(dec.pool.reshape(-1, 576)[int(wl.page_table[b, 0]) * wl.page_size, :512])
+        sum_abs = np.abs(dec.w_uv) @ z  # [H, 128]
+        bound = 2.0 ** -8 * np.abs(ref[b]) + 2.0 ** -20 * sum_abs + 1e-30
+        assert np.all(np.abs(got[b] - ref[b]) <= bound), f"sequence {b}"
+
+
+def test_decode_b64_fp8_sampled(B):
+    _say("decode_b64_fp8: generating")
+    wl = decode_recipe("decode_b64_fp8")
+    _say("decode_b64_fp8: running")
+    got = _run_decode(B, wl)
+    idx = [0, 31, 63]
+    _say("decode_b64_fp8: oracle on 3 sequences")
+    ref = oracle.decode(wl, batch_indices=idx)
+    assert np.isfinite(got).all()
+    _assert_close(got[idx], ref, FP8_MAX)
