@@ -96,21 +96,21 @@ int device_cu_count() {
   return n;
 }
 
-// Split workgroups over the batch: one per compute unit by default. Each
-// one's key range must span at most 1022 pages (the page-table window it
-// stages in LDS holds 1024 entries; a range may start mid-page and its first
-// tile is aligned down to 32 keys).
+// Split workgroups over the batch: one per compute unit by default. A range
+// of L keys starting mid-page, with its first tile aligned down to 32 keys,
+// spans at most (L + 30) / page_size + 2 pages, which must fit the page-table
+// window the kernel stages in LDS.
 int decode_groups(int B, int max_ctx, int page_size, int num_partitions) {
   int g = num_partitions > 0 ? num_partitions : device_cu_count();
   const long long keys = (long long)B * max_ctx;
-  const long long per_group = 1022LL * page_size - 64;
+  const long long per_group = (long long)(mla::kDecPageWindow - 2) * page_size - 64;
   const long long need = (keys + per_group - 1) / per_group;
   if (g < need) g = (int)need;
   return g;
 }
 
 // decode workspace: q_abs [B][H][576] bf16, cum [B+1] u32, wstart [G+1] u32,
-// wspan [B] int2, part_o [G+B][H][512] f32, part_ml [G+B][H][2] f32, o_lat
+// wspan [B] int2, wfirst [G] i32, part_o [G+B][64][H][8] f32, part_ml [G+B][H][2] f32, o_lat
 // [B][H][2][512] bf16 (hi, lo). G split workgroups cover the batch's
 // concatenated contexts in equal ranges.
 struct DecodeWs {
@@ -118,6 +118,7 @@ struct DecodeWs {
   uint32_t* cum;
   uint32_t* wstart;
   int2* wspan;
+  int32_t* wfirst;
   float* part_o;
   float* part_ml;
   uint16_t* o_lat;
@@ -138,6 +139,8 @@ DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
   off = align_up(off + (size_t)(w.G + 1) * sizeof(uint32_t));
   w.wspan = (int2*)(base + off);
   off = align_up(off + (size_t)B * sizeof(int2));
+  w.wfirst = (int32_t*)(base + off);
+  off = align_up(off + (size_t)w.G * sizeof(int32_t));
   w.part_o = (float*)(base + off);
   off = align_up(off + slots * H * mla::kLora * sizeof(float));
   w.part_ml = (float*)(base + off);
@@ -407,7 +410,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                       "absorb kernel");
   if (st != MLA_OK) return st;
   st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, ws.wstart,
-                                            ws.wspan, ws.G, stream),
+                                            ws.wspan, ws.wfirst, ws.G, stream),
                   "prefix kernel");
   if (st != MLA_OK) return st;
   mla::DecodeArgs a;
@@ -416,6 +419,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   a.page_table = page_table;
   a.cum = ws.cum;
   a.wstart = ws.wstart;
+  a.wfirst = ws.wfirst;
   a.part_o = ws.part_o;
   a.part_ml = ws.part_ml;
   a.B = batch_size;

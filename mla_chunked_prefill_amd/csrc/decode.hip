@@ -83,7 +83,7 @@ __global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
-// 2. split-KV attention over the latent cache (bf16 cache)
+// 2. split-KV attention over the latent cache
 // ---------------------------------------------------------------------------
 // Key ranges. The contexts laid end to end hold N keys; range w of G covers
 // keys [w*N/G, (w+1)*N/G), so every range streams the same number of rows
@@ -91,64 +91,64 @@ __global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* _
 // sequence it touches, into slot w + b (injective over the touching pairs, at
 // most G + B slots).
 //
-// One workgroup per range, four waves, one per SIMD; wave w owns heads
-// 32w .. 32w+31 completely: its absorbed queries (576 deep) stay in registers
-// and so does its unnormalised output O^T (512 dims x 32 heads, fp32), so no
-// score or output crosses between waves and each cache row is read from
-// memory once for all heads. Per tile of 32 keys a wave computes the scores
-// S^T = Z Q^T (keys x heads, 36 MFMA steps, mfma 32x32x16: each lane owns
-// one head and its softmax statistics are in-lane plus one exchange with the
-// lane 32 away) and accumulates O^T += Z^T P^T (16 dim blocks x 2 key steps),
-// reading Z^T straight from the row-major tile with transposed LDS reads.
-// Key rows are fed to the score MFMA in the order kappa (bits 2 and 3 of the
-// row index swapped), which makes the bf16 probabilities directly the B
-// operand of the value product.
+// One workgroup per range, eight waves, two per SIMD. Waves g and g + 4 form
+// a pair that owns heads 32g .. 32g+31; each cache row is read from memory once
+// for all heads. Per tile of 32 keys, wave half hd of the pair computes the
+// partial scores over depth 288 hd .. 288 hd + 287 (18 MFMA steps, mfma
+// 32x32x16: S^T = Z Q^T, keys x heads, each lane owns one head), the two
+// halves are exchanged through LDS and summed (in both waves, bit for bit the
+// same sum), both waves take the same softmax, and wave half hd accumulates
+// output dims 256 hd .. 256 hd + 255 (O^T += Z^T P^T, 8 dim blocks x 2 key
+// steps, Z^T read straight from the row-major tile with transposed LDS
+// reads). The pair's two waves sit on different halves of the work, so a SIMD
+// always holds a second wave to run while one waits. Key rows are fed to the
+// score MFMA in the order kappa (bits 2 and 3 of the row index swapped),
+// which makes the bf16 probabilities directly the B operand of the value
+// product.
 //
 // The softmax reference maximum of a segment is its first tile's maximum and
 // never moves, so the output accumulator is never rescaled. Probabilities
 // stay below 2^kDecSlack (far inside fp32 and bf16 range) unless a later
-// score exceeds the reference by more than kDecSlack log2 units; a wave that
+// score exceeds the reference by more than kDecSlack log2 units; a pair that
 // sees one marks its partial states, and the combine step recomputes them
 // against their exact maximum.
 //
 // Tiles are aligned to 32 keys of the sequence (keys of the first tile before
 // the range start are masked). When the page size is a multiple of 32 a tile
-// is 32 consecutive pool rows (36 KB in one piece) and its direct loads use
-// per-lane offsets fixed for the whole kernel; otherwise every row's pool slot
-// is looked up. Two LDS stages keep one tile in flight while another is
-// computed (a tile's compute outlasts the memory latency). The first 18 score
-// steps take the absorbed queries from registers, the last 18 from a table in
-// LDS (registers hold the output accumulator instead). A row keeps its 72
-// 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
-// the score reads (16 rows at one column) and the transposed reads (4 rows x
-// 64 bytes) touch distinct LDS banks.
-constexpr int kDecWaves = 4;
+// is 32 consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its
+// direct loads use per-lane offsets fixed for the whole kernel; otherwise
+// every row's pool slot is looked up. Two LDS stages keep one tile in flight
+// while another is computed. An e4m3 tile lands in one of two staging buffers
+// and is widened exactly into the single bf16 stage before use. A bf16 row
+// keeps its 72 16-byte chunks with the chunk index's low three bits XORed by
+// zswz(row), so the score reads (16 rows at one column) and the transposed
+// reads (4 rows x 64 bytes) touch distinct LDS banks. The absorbed queries of
+// a wave's depth half stay in registers except the last kQLdsSteps steps,
+// which come from a small per-wave table in LDS.
+constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBN = 32;                          // keys per tile
 constexpr int kZRowChunks = 72;                     // 16-byte chunks per row
 constexpr int kZRowB = kZRowChunks * 16;            // 1152 bytes
 constexpr int kZStageB = kDecBN * kZRowB;           // 36864 bytes
-constexpr int kZStages = 2;
 constexpr int kZLoads = kZStageB / 1024;            // 36 wave loads of 1 KB
-constexpr int kDmaPerWave = kZLoads / kDecWaves;    // 9
-constexpr int kPTWindow = 1024;                     // page-table entries staged per segment
-// the second half of every absorbed query (depth 288 .. 575) lives in LDS:
-// rows of 288 bf16 + 16 bytes (spreads consecutive heads over distinct banks)
-constexpr int kQLdsSteps = 18;                      // score steps whose B operand is in LDS
-constexpr int kQRegSteps = 36 - kQLdsSteps;
-constexpr int kQRowB = kQLdsSteps * 32 + 16;        // 592 bytes
-constexpr int kQTabB = 128 * kQRowB;
+constexpr int kZLoadsPerWave = (kZLoads + kDecWaves - 1) / kDecWaves;  // 5 (waves 4..7: 4)
+constexpr int kPTWindow = kDecPageWindow;           // page-table entries staged per segment
+constexpr int kHalfSteps = 18;                      // score steps per depth half
+constexpr int kQLdsSteps = 6;                       // of them, B operand from the LDS table
+constexpr int kQRegSteps = kHalfSteps - kQLdsSteps;
+constexpr int kQRowB = kQLdsSteps * 32 + 16;        // 144 bytes: heads on distinct banks
+constexpr int kQTabB = 32 * kQRowB;                 // per wave
+constexpr int kXchgB = 64 * 16 * 4;                 // 4 KB of partial scores per wave
 constexpr float kDecSlack = 64.0f;
-static_assert(kZLoads % kDecWaves == 0, "every wave issues the same loads");
-// e4m3 cache: a tile (32 rows of 576 bytes, rows kept as stored) is loaded
-// into one of two staging buffers behind the single bf16 stage, and widened
-// exactly into the bf16 stage (8 codes per thread and step) before use
+static_assert(kPTWindow == kDecThreads, "one page-table entry per thread");
+// e4m3 cache: rows kept as stored in the staging buffers
 constexpr int kF8RowB = kCache;                     // 576 bytes
 constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
 constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
+constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 3 (waves 2..7: 2)
 constexpr int kF8Units = kDecBN * kZRowChunks;      // 2304 groups of 8 codes per tile
-static_assert(kZStageB + 2 * kF8StageB <= kZStages * kZStageB, "staging fits the stages");
-static_assert(kF8Units % kDecThreads == 0, "every thread widens the same number of groups");
+static_assert(kZStageB + 2 * kF8StageB <= 2 * kZStageB, "staging fits the stages");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
 __device__ __forceinline__ int zswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
@@ -167,7 +167,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* lds_byte_ptr) {
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
 // lds + 16 l (lds is wave-uniform). Inline assembly keeps the compiler from
 // treating later LDS reads of other stages as dependent on it (it would wait
-// for every load in flight); the kernel orders these loads itself with
+// for every load in flight); the kernels order these loads themselves with
 // s_waitcnt vmcnt, counting in issue order, and barriers. The asm sets m0 on
 // every call; the kernels keep no value of their own in m0.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
@@ -202,9 +202,10 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
-  // second half of the absorbed queries (B operand of the last 18 score steps)
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[kQTabB];
+  // two bf16 stages, or one bf16 stage and two e4m3 staging buffers
+  __shared__ __attribute__((aligned(1024))) uint8_t sZ[2 * kZStageB];
+  __shared__ __attribute__((aligned(16))) uint8_t sX[kDecWaves * kXchgB];  // partial scores
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[kDecWaves * kQTabB];  // query table
   __shared__ int sPT[kPTWindow];
 
   const int w = blockIdx.x;
@@ -216,23 +217,27 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & 3;   // head group of the pair
+  const int hd = wave >> 2;   // depth half (scores) and dim half (output)
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int head = wave * 32 + l32;
+  const int head = grp * 32 + l32;
   const bool hvalid = head < a.H;
   const float sl2 = a.scale_log2;
   const uint8_t* cache = (const uint8_t*)a.cache;
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)sZ);
 
   // ---- per-lane LDS read offsets (bytes inside a stage) ----
-  // scores: row kappa, chunk hf + 2 ks; ks = 4c + r -> s_base[r] + 128 c
+  // scores: row kappa, step ks = 18 hd + 4 c + r reads chunk 2 ks + hf, at
+  // s_base[r] + 128 c
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   int s_base[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s_base[r] = kappa * kZRowB + zchunk(kappa, hf + 2 * r) * 16;
-  // transposed reads for key step ks, half t: row 16 ks + 8 (g16 / 2) + 4 t +
-  // L16 / 4, bytes 64 md + 32 (g16 & 1) + 8 (L16 & 3); md = 2c + pm ->
-  // tr_base[ks][t][pm] + 128 c
+  for (int r = 0; r < 4; ++r)
+    s_base[r] = kappa * kZRowB + zchunk(kappa, 2 * (kHalfSteps * hd + r) + hf) * 16;
+  // transposed reads for key step ks, half t, dim block md = 8 hd + 2 c + pm:
+  // row 16 ks + 8 (g16 / 2) + 4 t + L16 / 4, bytes 64 md + 32 (g16 & 1) +
+  // 8 (L16 & 3) -> tr_base[ks][t][pm] + 128 c
   const int g16 = lane >> 4, L16 = lane & 15;
   int tr_base[2][2][2];
 #pragma unroll
@@ -242,17 +247,16 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int pm = 0; pm < 2; ++pm) {
         const int row = 16 * ks + 8 * (g16 >> 1) + 4 * t + (L16 >> 2);
-        const int chunk = 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
+        const int chunk = 32 * hd + 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
         tr_base[ks][t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
       }
-  // direct loads: load j of this wave fills LDS chunks 64 (wave + 4 j) + lane,
-  // i.e. tile row rr, source chunk cc (the XOR is its own inverse); its byte
-  // offset in a contiguous tile is rr * 1152 + cc * 16
-  // (offsets below 36 KB: two per register)
-  uint32_t dma_pk[(kDmaPerWave + 1) / 2];
+  // direct loads (bf16): load p = wave + 8 j fills LDS chunks 64 p + lane, i.e.
+  // tile row rr, source chunk cc (the XOR is its own inverse); its byte offset
+  // in a contiguous tile is rr * 1152 + cc * 16 (below 36 KB: two per register)
+  uint32_t dma_pk[(kZLoadsPerWave + 1) / 2];
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const int pch = (wave + kDecWaves * j) * 64 + lane;
+  for (int j = 0; j < kZLoadsPerWave; ++j) {
+    const int pch = min(wave + kDecWaves * j, kZLoads - 1) * 64 + lane;
     const int rr = pch / kZRowChunks;
     const uint32_t off = (uint32_t)(rr * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16);
     if (j & 1) dma_pk[j >> 1] |= off << 16; else dma_pk[j >> 1] = off;
@@ -261,19 +265,11 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
   };
   const bool contiguous = (a.ps % kDecBN) == 0;
-  // LDS score steps: B operand = head row of the query table, chunk 2 r + hf
-  const int q_base = head * kQRowB + hf * 16;
+  uint8_t* const xown = sX + wave * kXchgB + lane * 16;          // partial score exchange
+  const uint8_t* const xpeer = sX + (wave ^ 4) * kXchgB + lane * 16;
+  uint8_t* const qtab = sQ + wave * kQTabB + l32 * kQRowB + hf * 16;
 
-  // first sequence touched: largest b with cum[b] <= s_lo
-  int b;
-  {
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cum[mid] <= s_lo) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-  }
+  int b = a.wfirst[w];  // first sequence the range touches
   uint32_t pos = s_lo;
   while (pos < s_hi) {
     const uint32_t seg_end = min(s_hi, a.cum[b + 1]);
@@ -282,16 +278,41 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     const int k1 = (int)(seg_end - a.cum[b]);
     const int kt0 = k0 & ~(kDecBN - 1);
     const int ntiles = (k1 - kt0 + kDecBN - 1) / kDecBN;
-    // the segment's page-table entries, staged in LDS once
     const int lp0 = kt0 / a.ps;
     const int npg = (k1 - 1) / a.ps - lp0 + 1;
-    __syncthreads();  // the previous segment is done with the page window and the stages
-    for (int i = tid; i < min(npg, kPTWindow); i += kDecThreads) {
-      const int lp = lp0 + i;
-      int pg = lp < a.maxp ? a.page_table[(size_t)b * a.maxp + lp] : 0;
-      sPT[i] = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
+    // absorbed queries of this wave's heads and depth half: the first
+    // kQRegSteps steps in registers, the rest in the wave's LDS table (row =
+    // head in the group); their loads go out together with the page-table
+    // loads below
+    bf16x8 qf[kQRegSteps];
+    u32x4 qt[kQLdsSteps];
+    {
+      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache +
+                             kHalfSteps * 16 * hd + hf * 8;
+#pragma unroll
+      for (int ks = 0; ks < kQRegSteps; ++ks) {
+        u32x4 v = hvalid ? *(const u32x4*)(qrow + ks * 16) : u32x4{0, 0, 0, 0};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int r = 0; r < kQLdsSteps; ++r)
+        qt[r] = hvalid ? *(const u32x4*)(qrow + (kQRegSteps + r) * 16) : u32x4{0, 0, 0, 0};
     }
-    __syncthreads();
+    // the segment's page-table entries, staged in LDS once (one per thread)
+    int pg = 0;
+    if (tid < npg) {
+      const int lp = lp0 + tid;
+      pg = lp < a.maxp ? a.page_table[(size_t)b * a.maxp + lp] : 0;
+    }
+    __syncthreads();  // the previous segment is done with the page window, stages and tables
+    if (tid < npg) sPT[tid] = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
+#pragma unroll
+    for (int r = 0; r < kQLdsSteps; ++r) *(u32x4*)(qtab + r * 32) = qt[r];
+    __syncthreads();  // page window and query tables written
+    // wait for q here, before any tile load is in flight: the compiler cannot
+    // count the tile loads, so a wait it placed for q inside the tile loop
+    // would drain them every tile (gfx9 encoding: vmcnt 0, others unlimited)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     // loads of tile t (keys kt0 + 32 t ..) into stage st
     const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
@@ -306,7 +327,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
           const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
           const void* sb = uniform_ptr_d(cache + slot * kF8RowB);
 #pragma unroll
-          for (int j = 0; j < (kF8Loads + kDecWaves - 1) / kDecWaves; ++j)
+          for (int j = 0; j < kF8LoadsPerWave; ++j)
             if (wave + kDecWaves * j < kF8Loads)
               dma16_s(sb, (uint32_t)((wave + kDecWaves * j) * 1024 + lane * 16),
                       base + (wave + kDecWaves * j) * 1024);
@@ -314,14 +335,13 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
           const int key = min(kt + (lane & 31), k1 - 1);
           const int lp = key / a.ps;
           const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
-#pragma unroll
-          for (int j = 0; j < (kF8Loads + kDecWaves - 1) / kDecWaves; ++j) {
-            const int p = (wave + kDecWaves * j) * 64 + lane;
-            const int rr = p / (kF8RowB / 16);
+          // one load at a time keeps this rarely taken path's registers few
+#pragma unroll 1
+          for (int p = wave; p < kF8Loads; p += kDecWaves) {
+            const int pch = p * 64 + lane;
+            const int rr = pch / (kF8RowB / 16);
             const int rs = __shfl(slot, rr, 64);
-            if (wave + kDecWaves * j < kF8Loads)
-              dma16(cache + (size_t)rs * kF8RowB + (p - rr * (kF8RowB / 16)) * 16,
-                    base + (wave + kDecWaves * j) * 1024);
+            dma16(cache + (size_t)rs * kF8RowB + (pch - rr * (kF8RowB / 16)) * 16, base + p * 1024);
           }
         }
         return;
@@ -334,113 +354,98 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
         const void* sb = uniform_ptr_d(cache + slot * kZRowB);
 #pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j)
-          dma16_s(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+        for (int j = 0; j < kZLoadsPerWave; ++j)
+          if (wave + kDecWaves * j < kZLoads)
+            dma16_s(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
       } else {
         // pool slot of tile row (lane & 31); rows past the segment read its last
         // row (a context row whose page is inside the staged window)
         const int key = min(kt + (lane & 31), k1 - 1);
         const int lp = key / a.ps;
         const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
-        int rs[kDmaPerWave];
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-          const int rr = ((wave + kDecWaves * j) * 64 + lane) / kZRowChunks;
-          rs[j] = __shfl(slot, rr, 64);
-        }
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-          const int rr = ((wave + kDecWaves * j) * 64 + lane) / kZRowChunks;
-          dma16(cache + (size_t)rs[j] * kZRowB + (dma_off(j) - rr * kZRowB),
-                base + (wave + kDecWaves * j) * 1024);
+        // one load at a time keeps this rarely taken path's registers few
+#pragma unroll 1
+        for (int p = wave; p < kZLoads; p += kDecWaves) {
+          const int pch = p * 64 + lane;
+          const int rr = pch / kZRowChunks;
+          const int rs = __shfl(slot, rr, 64);
+          dma16(cache + (size_t)rs * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16,
+                base + p * 1024);
         }
       }
     };
 
-    // absorbed queries of this wave's heads: score steps 0 .. 17 in
-    // registers, 18 .. 35 in the LDS table (row = head)
-    bf16x8 qf[kQRegSteps];
-    {
-      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache;
+    f32x16 o[8];
 #pragma unroll
-      for (int ks = 0; ks < kQRegSteps; ++ks) {
-        u32x4 v = hvalid ? *(const u32x4*)(qrow + ks * 16 + hf * 8) : u32x4{0, 0, 0, 0};
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
-      }
-      // table row of this lane's head: 36 chunks, this lane copies chunks hf, hf + 2, ..
-#pragma unroll
-      for (int r = 0; r < kQLdsSteps; ++r) {
-        const int ch = 2 * r + hf;
-        u32x4 v = hvalid ? *(const u32x4*)(qrow + kQRegSteps * 16 + ch * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sQ + head * kQRowB + ch * 16) = v;
-      }
-    }
-    __syncthreads();  // the query table is written
-    // wait for q here, before any tile load is in flight: the compiler cannot
-    // count the tile loads, so a wait it placed for q inside the tile loop
-    // would drain them every tile (gfx9 encoding: vmcnt 0, others unlimited)
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    f32x16 o[16];
-#pragma unroll
-    for (int md = 0; md < 16; ++md)
+    for (int md = 0; md < 8; ++md)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
     float m_ref = -INFINITY;   // reference maximum (log2 domain): the first tile's
     float m_seen = -INFINITY;  // largest scaled score of the segment
     float l_run = 0.f;
-    bool halted = false;       // wave-uniform: the partial is marked for recomputation
+    bool halted = false;       // wave-uniform (and equal in both waves of a pair)
 
     issue(0, 0);  // ntiles >= 1
 
     for (int t = 0; t < ntiles; ++t) {
       // wait for this wave's loads of tile t (the only ones in flight)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      static_assert(kZStages == 2, "one tile in flight");
       // tile t landed for every wave; every wave is done with tile t-1 (its
-      // bf16 stage, and for e4m3 the staging buffer of tile t+1)
+      // bf16 stage, the score exchange, and for e4m3 the staging buffer of
+      // tile t+1)
       __syncthreads();
       if (t + 1 < ntiles) issue(t + 1, (t + 1) % 2);
       const uint8_t* Z = sZ + (kFp8 ? 0 : (t % 2) * kZStageB);
       if constexpr (kFp8) {
         const uint8_t* F = sZ + kZStageB + (t % 2) * kF8StageB;
 #pragma unroll
-        for (int i = 0; i < kF8Units / kDecThreads; ++i) {
+        for (int i = 0; i < (kF8Units + kDecThreads - 1) / kDecThreads; ++i) {
           const int u = tid + kDecThreads * i;  // row u / 72, bf16 chunk u % 72
-          const int r = u / kZRowChunks, c = u - r * kZRowChunks;
-          const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
-          *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
+          if (u < kF8Units) {
+            const int r = u / kZRowChunks, c = u - r * kZRowChunks;
+            const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
+            *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
+          }
         }
         __syncthreads();  // the bf16 tile is complete
       }
       const int kt = kt0 + t * kDecBN;
 
-      // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
-      f32x16 s, s2;
+      // ---- partial S^T over this wave's depth half: 32 keys x 32 heads ----
+      f32x16 s;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.f; s2[i] = 0.f; }
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 36; ks += 2) {
+      for (int ks = 0; ks < kHalfSteps; ++ks) {
         const bf16x8 za = *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
-        const bf16x8 zb = *(const bf16x8*)(Z + s_base[(ks + 1) & 3] + 128 * ((ks + 1) >> 2));
         const bf16x8 qa = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0]
-                                          : *(const bf16x8*)(sQ + q_base + 32 * (ks - kQRegSteps));
-        const bf16x8 qb = ks + 1 < kQRegSteps
-                              ? qf[ks + 1 < kQRegSteps ? ks + 1 : 0]
-                              : *(const bf16x8*)(sQ + q_base + 32 * (ks + 1 - kQRegSteps));
+                                          : *(const bf16x8*)(qtab + 32 * (ks - kQRegSteps));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qa, s, 0, 0, 0);
-        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, qb, s2, 0, 0, 0);
       }
-      // LDS operands run about four MFMAs ahead: step i needs the key
-      // fragment (and from step 18 on the query fragment too)
+      // LDS operands run about four MFMAs ahead
       __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
 #pragma unroll
-      for (int i = 0; i < 36; ++i) {
+      for (int i = 0; i < kHalfSteps; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
-        if (i < 14) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
-        else if (i < 32) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
+        if (i < kQRegSteps - 4) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
+        else if (i < kHalfSteps - 4) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
       }
+      // exchange the partial scores with the other wave of the pair (lane l of
+      // both waves holds the same keys and heads)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] += s2[i];
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = s[4 * g + j];
+        *(f32x4*)(xown + g * 1024) = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 v = *(const f32x4*)(xpeer + g * 1024);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[4 * g + j] += v[j];
+      }
 
       // register i holds tile row 16*(i/8) + 8*hf + i%8
       if (kt < k0 || kt + kDecBN > k1) {
@@ -475,9 +480,9 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       }
       l_run += sum_with_lane32(psum);
 
-      // ---- O^T[512 dims x 32 heads] += Z^T P^T ----
+      // ---- O^T[this wave's 256 dims x 32 heads] += Z^T P^T ----
 #pragma unroll
-      for (int md = 0; md < 16; ++md)
+      for (int md = 0; md < 8; ++md)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const bf16x4 a0 = ds_read_tr16(Z + tr_base[ks][0][md & 1] + 128 * (md >> 1));
@@ -488,28 +493,30 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       // transposed reads eight ahead (four MFMAs) of the value product
       __builtin_amdgcn_sched_group_barrier(0x0100, 8, 1);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);
-        if (i < 28) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
       }
     }
 
-    // partial state of (w, b): slot w + b
+    // partial state of (w, b): slot w + b. The output is stored by groups of
+    // eight dims, [slot][dim / 8][head][dim % 8], so that every store
+    // instruction writes 1 KB in one piece (32 heads x 32 bytes).
     if (hvalid) {
       const size_t base = ((size_t)(w + b) * a.H + head);
-      float* op = a.part_o + base * kLora;
-      // O^T register i of block md: dim 32*md + 8*(i/4) + 4*hf + i%4
+      // O^T register i of block md: dim 256 hd + 32 md + 8 (i / 4) + 4 hf + i % 4
+      float* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
 #pragma unroll
-      for (int md = 0; md < 16; ++md)
+      for (int md = 0; md < 8; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
-          *(f32x4*)(op + md * 32 + g * 8 + hf * 4) = v;
+          *(f32x4*)(op + (size_t)(32 * hd + 4 * md + g) * a.H * 8) = v;
         }
-      if (hf == 0) {
-        // a wave whose scores outgrew the reference hands (exact maximum, -1)
+      if (hd == 0 && hf == 0) {
+        // a pair whose scores outgrew the reference hands (exact maximum, -1)
         // to the combine step, which recomputes this partial against it
         a.part_ml[base * 2 + 0] = halted ? m_seen : m_ref;
         a.part_ml[base * 2 + 1] = halted ? -1.0f : l_run;
@@ -525,7 +532,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const uint32_t* ctx,
                                                             int B, uint32_t* wstart, int2* wspan,
-                                                            int G) {
+                                                            int32_t* wfirst, int G) {
   __shared__ uint32_t s_scan[256];
   __shared__ uint32_t s_carry;
   const int tid = threadIdx.x;
@@ -553,6 +560,16 @@ __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const
   for (int w = tid; w <= G; w += 256) wstart[w] = (uint32_t)(((uint64_t)w * N) / G);
   __threadfence();  // other threads of the workgroup read these entries below
   __syncthreads();
+  // first sequence of every key range: largest b with cum[b] <= wstart[w]
+  for (int w = tid; w < G; w += 256) {
+    const uint32_t key = wstart[w];
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    wfirst[w] = lo;
+  }
   // ranges holding sequence b's first and last keys (empty sequences: (0, -1))
   for (int b = tid; b < B; b += 256) {
     const uint32_t lo_key = cum[b], hi_key = cum[b + 1];
@@ -650,8 +667,9 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
       if (l < 0.f) {  // marked partial: recompute (wave-uniform)
         recompute_partial(c, w, b, h, m, ow, l);
       } else {
-        const f32x4 v0 = *(const f32x4*)(c.part_o + base * kLora + 8 * lane);
-        const f32x4 v1 = *(const f32x4*)(c.part_o + base * kLora + 8 * lane + 4);
+        const float* po = c.part_o + (((size_t)(w + b) * (kLora / 8) + lane) * c.H + h) * 8;
+        const f32x4 v0 = *(const f32x4*)(po);
+        const f32x4 v1 = *(const f32x4*)(po + 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) { ow[j] = v0[j]; ow[4 + j] = v1[j]; }
       }
@@ -694,9 +712,9 @@ hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16
 }
 
 hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, uint32_t* wstart,
-                                int2* wspan, int G, hipStream_t stream) {
+                                int2* wspan, int32_t* wfirst, int G, hipStream_t stream) {
   hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, B, wstart,
-                     wspan, G);
+                     wspan, wfirst, G);
   return hipGetLastError();
 }
 

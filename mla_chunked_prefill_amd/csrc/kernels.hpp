@@ -43,20 +43,24 @@ struct AttnArgs {
   int n_slots, B, H, max_rows;
   float scale_log2;
 };
+// Page-table entries the split-KV kernel stages in LDS per segment; the host
+// sizes key ranges so that a segment never spans more pages.
+constexpr int kDecPageWindow = 512;
 struct DecodeArgs {
   const uint16_t* q_abs;     // [B][H][576] bf16
   const void* cache;         // [num_pages][ps][576] bf16 or e4m3fn
   const int32_t* page_table; // [B][maxp]
   const uint32_t* cum;       // [B+1] prefix sums of the context lengths
   const uint32_t* wstart;    // [G+1] first key of every key range
-  float* part_o;             // [G + B][H][512]
+  const int32_t* wfirst;     // [G] first sequence every key range touches
+  float* part_o;             // [G + B][512 / 8][H][8]: dims by groups of 8
   float* part_ml;            // [G + B][H][2]
   int B, H, ps, maxp, num_pages, G;
   float scale_log2;
 };
 struct CombineArgs {
   uint16_t* o_lat;           // [B][H][2][512] bf16: hi then lo
-  float* part_o;             // [G + B][H][512]
+  float* part_o;             // [G + B][512 / 8][H][8]
   float* part_ml;            // [G + B][H][2] (max in the log2 domain, sum; a
                              // negative sum marks a partial to recompute)
   const uint32_t* cum;       // [B+1]
@@ -79,8 +83,8 @@ hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
 hipError_t launch_decode_absorb(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                 hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
-hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, uint32_t*, int2*, int,
-                                hipStream_t);
+hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, uint32_t*, int2*, int32_t*,
+                                int, hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);
