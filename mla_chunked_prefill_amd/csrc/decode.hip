@@ -91,64 +91,64 @@ __global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* _
 // sequence it touches, into slot w + b (injective over the touching pairs, at
 // most G + B slots).
 //
-// One workgroup per range, eight waves, two per SIMD. Waves g and g + 4 form
-// a pair that owns heads 32g .. 32g+31; each cache row is read from memory once
-// for all heads. Per tile of 32 keys, wave half hd of the pair computes the
-// partial scores over depth 288 hd .. 288 hd + 287 (18 MFMA steps, mfma
-// 32x32x16: S^T = Z Q^T, keys x heads, each lane owns one head), the two
-// halves are exchanged through LDS and summed (in both waves, bit for bit the
-// same sum), both waves take the same softmax, and wave half hd accumulates
-// output dims 256 hd .. 256 hd + 255 (O^T += Z^T P^T, 8 dim blocks x 2 key
-// steps, Z^T read straight from the row-major tile with transposed LDS
-// reads). The pair's two waves sit on different halves of the work, so a SIMD
-// always holds a second wave to run while one waits. Key rows are fed to the
-// score MFMA in the order kappa (bits 2 and 3 of the row index swapped),
-// which makes the bf16 probabilities directly the B operand of the value
-// product.
+// One workgroup per range, four waves, one per SIMD; wave w owns heads
+// 32w .. 32w+31 completely: its absorbed queries (576 deep, 144 registers)
+// and its unnormalised output O^T (512 dims x 32 heads fp32, held in the
+// accumulation registers) stay resident, so no score or output crosses
+// between waves and each cache row is read from memory once for all heads.
+// Per tile of 32 keys a wave computes S^T = Z Q^T (keys x heads, 36 MFMA
+// steps of mfma 32x32x16 in two accumulation chains; each lane owns one head,
+// its softmax statistics are in-lane plus one exchange with the lane 32
+// away) and accumulates O^T += Z^T P^T (16 dim blocks x 2 key steps), reading
+// Z^T straight from the row-major tile with transposed LDS reads. Key rows
+// are fed to the score MFMA in the order kappa (bits 2 and 3 of the row index
+// swapped), which makes the bf16 probabilities directly the B operand of the
+// value product. LDS operands are read four MFMAs ahead into rotating
+// registers.
 //
 // The softmax reference maximum of a segment is its first tile's maximum and
 // never moves, so the output accumulator is never rescaled. Probabilities
 // stay below 2^kDecSlack (far inside fp32 and bf16 range) unless a later
-// score exceeds the reference by more than kDecSlack log2 units; a pair that
+// score exceeds the reference by more than kDecSlack log2 units; a wave that
 // sees one marks its partial states, and the combine step recomputes them
 // against their exact maximum.
 //
 // Tiles are aligned to 32 keys of the sequence (keys of the first tile before
-// the range start are masked). When the page size is a multiple of 32 a tile
-// is 32 consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its
-// direct loads use per-lane offsets fixed for the whole kernel; otherwise
-// every row's pool slot is looked up. Two LDS stages keep one tile in flight
-// while another is computed. An e4m3 tile lands in one of two staging buffers
-// and is widened exactly into the single bf16 stage before use. A bf16 row
-// keeps its 72 16-byte chunks with the chunk index's low three bits XORed by
-// zswz(row), so the score reads (16 rows at one column) and the transposed
-// reads (4 rows x 64 bytes) touch distinct LDS banks. The absorbed queries of
-// a wave's depth half stay in registers except the last kQLdsSteps steps,
-// which come from a small per-wave table in LDS.
-constexpr int kDecWaves = 8;
+// the range start are masked). Four LDS stages hold tiles t .. t+3: the loads
+// of tile t+3 go out while tile t is computed, three tiles ahead of use, one
+// barrier per tile. When the page size is a multiple of 32 a tile is 32
+// consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its direct
+// loads are spread between the score MFMAs; otherwise every row's pool slot
+// is looked up and the loads go out in one burst. A bf16 row keeps its 72
+// 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
+// the score reads (16 rows at one column) and the transposed reads (4 rows x
+// 64 bytes) touch distinct LDS banks. An e4m3 tile lands, rows as stored, in
+// one of four staging buffers and is widened exactly into the single bf16
+// stage before use.
+constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBN = 32;                          // keys per tile
 constexpr int kZRowChunks = 72;                     // 16-byte chunks per row
 constexpr int kZRowB = kZRowChunks * 16;            // 1152 bytes
 constexpr int kZStageB = kDecBN * kZRowB;           // 36864 bytes
+constexpr int kZStages = 4;
 constexpr int kZLoads = kZStageB / 1024;            // 36 wave loads of 1 KB
-constexpr int kZLoadsPerWave = (kZLoads + kDecWaves - 1) / kDecWaves;  // 5 (waves 4..7: 4)
+constexpr int kZLoadsPerWave = kZLoads / kDecWaves; // 9
 constexpr int kPTWindow = kDecPageWindow;           // page-table entries staged per segment
-constexpr int kHalfSteps = 18;                      // score steps per depth half
-constexpr int kQLdsSteps = 6;                       // of them, B operand from the LDS table
-constexpr int kQRegSteps = kHalfSteps - kQLdsSteps;
-constexpr int kQRowB = kQLdsSteps * 32 + 16;        // 144 bytes: heads on distinct banks
-constexpr int kQTabB = 32 * kQRowB;                 // per wave
-constexpr int kXchgB = 64 * 16 * 4;                 // 4 KB of partial scores per wave
+constexpr int kQSteps = kCache / 16;                // 36 score steps
 constexpr float kDecSlack = 64.0f;
-static_assert(kPTWindow == kDecThreads, "one page-table entry per thread");
 // e4m3 cache: rows kept as stored in the staging buffers
 constexpr int kF8RowB = kCache;                     // 576 bytes
 constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
+constexpr int kF8Stages = 4;
 constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
-constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 3 (waves 2..7: 2)
+constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 5 (waves 2, 3: 4)
 constexpr int kF8Units = kDecBN * kZRowChunks;      // 2304 groups of 8 codes per tile
-static_assert(kZStageB + 2 * kF8StageB <= 2 * kZStageB, "staging fits the stages");
+static_assert(kZLoads % kDecWaves == 0, "even bf16 loads per wave");
+static_assert(kF8Loads == 4 * kDecWaves + 2, "e4m3: waves 0, 1 load five times, waves 2, 3 four");
+static_assert(kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
+static_assert(kF8Units % kDecThreads == 0, "even widening per thread");
+static_assert(kPTWindow % kDecThreads == 0, "even page-table staging per thread");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
 __device__ __forceinline__ int zswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
@@ -164,23 +164,25 @@ __device__ __forceinline__ bf16x4 ds_read_tr16(const uint8_t* lds_byte_ptr) {
   return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte_ptr)));
 }
 
-// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
-// lds + 16 l (lds is wave-uniform). Inline assembly keeps the compiler from
-// treating later LDS reads of other stages as dependent on it (it would wait
-// for every load in flight); the kernels order these loads themselves with
+// Direct global -> LDS loads: lane l's 16 bytes land at lds + 16 l; lds is
+// wave-uniform. Inline assembly keeps the compiler from
+// treating later LDS reads of other stages as dependent on them (it would
+// wait for every load in flight); the kernel orders these loads itself with
 // s_waitcnt vmcnt, counting in issue order, and barriers. The asm sets m0 on
-// every call; the kernels keep no value of their own in m0.
+// every call; the kernels keep no value of their own in m0. The variants
+// without a compiler memory barrier are issued between the score MFMAs of
+// another stage, where the kernel never touches the target stage.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds), "v"(src)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma16_s_nb(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+               : "m0");
 }
 __device__ __forceinline__ const void* uniform_ptr_d(const void* p) {
   const uint64_t v = (uint64_t)p;
@@ -202,11 +204,12 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
-  // two bf16 stages, or one bf16 stage and two e4m3 staging buffers
-  __shared__ __attribute__((aligned(1024))) uint8_t sZ[2 * kZStageB];
-  __shared__ __attribute__((aligned(16))) uint8_t sX[kDecWaves * kXchgB];  // partial scores
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[kDecWaves * kQTabB];  // query table
+  // bf16: four stages; e4m3: one bf16 stage and four staging buffers behind it
+  __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
   __shared__ int sPT[kPTWindow];
+  constexpr int kLoadsPerWave = kFp8 ? kF8LoadsPerWave : kZLoadsPerWave;
+  constexpr int kStageB = kFp8 ? kF8StageB : kZStageB;
+  constexpr int kStage0 = kFp8 ? kZStageB : 0;        // byte offset of load stage 0
 
   const int w = blockIdx.x;
   if (w >= a.G) return;
@@ -217,57 +220,51 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave & 3;   // head group of the pair
-  const int hd = wave >> 2;   // depth half (scores) and dim half (output)
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int head = grp * 32 + l32;
+  const int head = wave * 32 + l32;
   const bool hvalid = head < a.H;
   const float sl2 = a.scale_log2;
   const uint8_t* cache = (const uint8_t*)a.cache;
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)sZ);
 
   // ---- per-lane LDS read offsets (bytes inside a stage) ----
-  // scores: row kappa, step ks = 18 hd + 4 c + r reads chunk 2 ks + hf, at
-  // s_base[r] + 128 c
+  // scores: row kappa, step ks = 4c + r reads chunk 2 ks + hf at s_base[r] + 128 c
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   int s_base[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    s_base[r] = kappa * kZRowB + zchunk(kappa, 2 * (kHalfSteps * hd + r) + hf) * 16;
-  // transposed reads for key step ks, half t, dim block md = 8 hd + 2 c + pm:
-  // row 16 ks + 8 (g16 / 2) + 4 t + L16 / 4, bytes 64 md + 32 (g16 & 1) +
-  // 8 (L16 & 3) -> tr_base[ks][t][pm] + 128 c
+  for (int r = 0; r < 4; ++r) s_base[r] = kappa * kZRowB + zchunk(kappa, 2 * r + hf) * 16;
+  // transposed reads for key step ks, half t, dim block md = 2 c + pm: row
+  // 16 ks + 8 (g16 / 2) + 4 t + L16 / 4, bytes 64 md + 32 (g16 & 1) +
+  // 8 (L16 & 3) -> tr_base[t][pm] + 18432 ks + 128 c (the swizzle ignores
+  // row bit 4)
   const int g16 = lane >> 4, L16 = lane & 15;
-  int tr_base[2][2][2];
+  int tr_base[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int pm = 0; pm < 2; ++pm) {
-        const int row = 16 * ks + 8 * (g16 >> 1) + 4 * t + (L16 >> 2);
-        const int chunk = 32 * hd + 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
-        tr_base[ks][t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
-      }
-  // direct loads (bf16): load p = wave + 8 j fills LDS chunks 64 p + lane, i.e.
-  // tile row rr, source chunk cc (the XOR is its own inverse); its byte offset
-  // in a contiguous tile is rr * 1152 + cc * 16 (below 36 KB: two per register)
+    for (int pm = 0; pm < 2; ++pm) {
+      const int row = 8 * (g16 >> 1) + 4 * t + (L16 >> 2);
+      const int chunk = 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
+      tr_base[t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
+    }
+  // direct loads of a contiguous bf16 tile: load j of this wave (p = wave +
+  // 4 j) fills LDS chunks 64 p + lane, i.e. tile row rr, source chunk
+  // zchunk(rr, cc) (the XOR is its own inverse); byte offsets below 36 KB,
+  // two per register. e4m3: load p covers bytes 1024 p + 16 lane as stored.
   uint32_t dma_pk[(kZLoadsPerWave + 1) / 2];
 #pragma unroll
   for (int j = 0; j < kZLoadsPerWave; ++j) {
-    const int pch = min(wave + kDecWaves * j, kZLoads - 1) * 64 + lane;
+    const int pch = (wave + kDecWaves * j) * 64 + lane;
     const int rr = pch / kZRowChunks;
     const uint32_t off = (uint32_t)(rr * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16);
     if (j & 1) dma_pk[j >> 1] |= off << 16; else dma_pk[j >> 1] = off;
   }
   auto dma_off = [&](int j) __attribute__((always_inline)) {
-    return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    if constexpr (kFp8) return (uint32_t)((wave + kDecWaves * j) * 1024 + lane * 16);
+    else return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
   };
   const bool contiguous = (a.ps % kDecBN) == 0;
-  uint8_t* const xown = sX + wave * kXchgB + lane * 16;          // partial score exchange
-  const uint8_t* const xpeer = sX + (wave ^ 4) * kXchgB + lane * 16;
-  uint8_t* const qtab = sQ + wave * kQTabB + l32 * kQRowB + hf * 16;
 
   int b = a.wfirst[w];  // first sequence the range touches
   uint32_t pos = s_lo;
@@ -278,174 +275,171 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     const int k1 = (int)(seg_end - a.cum[b]);
     const int kt0 = k0 & ~(kDecBN - 1);
     const int ntiles = (k1 - kt0 + kDecBN - 1) / kDecBN;
+    const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
     const int lp0 = kt0 / a.ps;
     const int npg = (k1 - 1) / a.ps - lp0 + 1;
-    // absorbed queries of this wave's heads and depth half: the first
-    // kQRegSteps steps in registers, the rest in the wave's LDS table (row =
-    // head in the group); their loads go out together with the page-table
-    // loads below
-    bf16x8 qf[kQRegSteps];
-    u32x4 qt[kQLdsSteps];
+    // absorbed queries of this wave's heads, all 36 score steps; their loads
+    // go out together with the page-table loads below
+    bf16x8 qf[kQSteps];
     {
-      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache +
-                             kHalfSteps * 16 * hd + hf * 8;
+      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache + hf * 8;
 #pragma unroll
-      for (int ks = 0; ks < kQRegSteps; ++ks) {
+      for (int ks = 0; ks < kQSteps; ++ks) {
         u32x4 v = hvalid ? *(const u32x4*)(qrow + ks * 16) : u32x4{0, 0, 0, 0};
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
-#pragma unroll
-      for (int r = 0; r < kQLdsSteps; ++r)
-        qt[r] = hvalid ? *(const u32x4*)(qrow + (kQRegSteps + r) * 16) : u32x4{0, 0, 0, 0};
     }
-    // the segment's page-table entries, staged in LDS once (one per thread)
-    int pg = 0;
-    if (tid < npg) {
-      const int lp = lp0 + tid;
-      pg = lp < a.maxp ? a.page_table[(size_t)b * a.maxp + lp] : 0;
-    }
-    __syncthreads();  // the previous segment is done with the page window, stages and tables
-    if (tid < npg) sPT[tid] = (pg < 0 || pg >= a.num_pages) ? 0 : pg;
+    // the segment's page-table entries, staged in LDS once
+    int pg[kPTWindow / kDecThreads];
 #pragma unroll
-    for (int r = 0; r < kQLdsSteps; ++r) *(u32x4*)(qtab + r * 32) = qt[r];
-    __syncthreads();  // page window and query tables written
+    for (int i = 0; i < kPTWindow / kDecThreads; ++i) {
+      const int e = tid + kDecThreads * i;
+      const int lp = lp0 + e;
+      pg[i] = (e < npg && lp < a.maxp) ? a.page_table[(size_t)b * a.maxp + lp] : 0;
+    }
+    __syncthreads();  // the previous segment is done with the page window and the stages
+#pragma unroll
+    for (int i = 0; i < kPTWindow / kDecThreads; ++i)
+      sPT[tid + kDecThreads * i] = (pg[i] < 0 || pg[i] >= a.num_pages) ? 0 : pg[i];
+    __syncthreads();  // page window written
     // wait for q here, before any tile load is in flight: the compiler cannot
     // count the tile loads, so a wait it placed for q inside the tile loop
-    // would drain them every tile (gfx9 encoding: vmcnt 0, others unlimited)
+    // would drain them (gfx9 encoding: vmcnt 0, others unlimited)
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // loads of tile t (keys kt0 + 32 t ..) into stage st
-    const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
-    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+    // pool slot of key (lp0 is the window's first page)
+    auto slot_of = [&](int key) __attribute__((always_inline)) {
+      const int lp = key / a.ps;
+      return sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+    };
+    // tile t (keys kt0 + 32 t ..) can be loaded in one piece when the page
+    // holds the whole tile and every row of it is a context row
+    auto one_piece = [&](int t) __attribute__((always_inline)) {
+      return contiguous && kt0 + (t + 1) * kDecBN <= ctx_b;
+    };
+    // all loads of tile t into load stage t % 4, in one burst
+    auto issue = [&](int t) __attribute__((always_inline)) {
       const int kt = kt0 + t * kDecBN;
-      if constexpr (kFp8) {
-        // staging st holds the tile's rows as stored: load p (of 1152) of 16
-        // bytes covers bytes 16 p, i.e. row p / 36, bytes 16 (p % 36) of it
-        const uint32_t base = lds0 + kZStageB + st * kF8StageB;
-        if (contiguous && kt + kDecBN <= ctx_b) {
-          const int lp = kt / a.ps;
-          const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
-          const void* sb = uniform_ptr_d(cache + slot * kF8RowB);
+      const uint32_t base = lds0 + kStage0 + (t % 4) * kStageB;
+      if (one_piece(t)) {
+        const void* sb = uniform_ptr_d(cache + (size_t)slot_of(kt) * (kFp8 ? kF8RowB : kZRowB));
 #pragma unroll
-          for (int j = 0; j < kF8LoadsPerWave; ++j)
-            if (wave + kDecWaves * j < kF8Loads)
-              dma16_s(sb, (uint32_t)((wave + kDecWaves * j) * 1024 + lane * 16),
-                      base + (wave + kDecWaves * j) * 1024);
-        } else {
-          const int key = min(kt + (lane & 31), k1 - 1);
-          const int lp = key / a.ps;
-          const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
-          // one load at a time keeps this rarely taken path's registers few
-#pragma unroll 1
-          for (int p = wave; p < kF8Loads; p += kDecWaves) {
-            const int pch = p * 64 + lane;
-            const int rr = pch / (kF8RowB / 16);
-            const int rs = __shfl(slot, rr, 64);
-            dma16(cache + (size_t)rs * kF8RowB + (pch - rr * (kF8RowB / 16)) * 16, base + p * 1024);
-          }
-        }
-        return;
-      }
-      const uint32_t base = lds0 + st * kZStageB;
-      // one contiguous piece when the page holds the whole tile and every row
-      // of it is a context row (rows past the context are never read)
-      if (contiguous && kt + kDecBN <= ctx_b) {
-        const int lp = kt / a.ps;
-        const size_t slot = (size_t)sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (kt - lp * a.ps);
-        const void* sb = uniform_ptr_d(cache + slot * kZRowB);
-#pragma unroll
-        for (int j = 0; j < kZLoadsPerWave; ++j)
-          if (wave + kDecWaves * j < kZLoads)
-            dma16_s(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+        for (int j = 0; j < kLoadsPerWave; ++j)
+          if (!kFp8 || wave + kDecWaves * j < kF8Loads)
+            dma16_s_nb(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+        asm volatile("" ::: "memory");
       } else {
         // pool slot of tile row (lane & 31); rows past the segment read its last
-        // row (a context row whose page is inside the staged window)
-        const int key = min(kt + (lane & 31), k1 - 1);
-        const int lp = key / a.ps;
-        const int slot = sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
-        // one load at a time keeps this rarely taken path's registers few
+        // row (a context row whose page is inside the staged window). One load
+        // at a time keeps this rarely taken path's registers few.
+        const int slot = slot_of(min(kt + (lane & 31), k1 - 1));
 #pragma unroll 1
-        for (int p = wave; p < kZLoads; p += kDecWaves) {
-          const int pch = p * 64 + lane;
-          const int rr = pch / kZRowChunks;
-          const int rs = __shfl(slot, rr, 64);
-          dma16(cache + (size_t)rs * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16,
-                base + p * 1024);
+        for (int p = wave; p < (kFp8 ? kF8Loads : kZLoads); p += kDecWaves) {
+          if constexpr (kFp8) {
+            const int byte = p * 1024 + lane * 16;
+            const int rr = byte / kF8RowB;
+            const int rs = __shfl(slot, rr, 64);
+            dma16(cache + (size_t)rs * kF8RowB + (byte - rr * kF8RowB), base + p * 1024);
+          } else {
+            const int pch = p * 64 + lane;
+            const int rr = pch / kZRowChunks;
+            const int rs = __shfl(slot, rr, 64);
+            dma16(cache + (size_t)rs * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16,
+                  base + p * 1024);
+          }
         }
       }
     };
 
-    f32x16 o[8];
+    f32x16 o[16];
 #pragma unroll
-    for (int md = 0; md < 8; ++md)
+    for (int md = 0; md < 16; ++md)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
     float m_ref = -INFINITY;   // reference maximum (log2 domain): the first tile's
     float m_seen = -INFINITY;  // largest scaled score of the segment
     float l_run = 0.f;
-    bool halted = false;       // wave-uniform (and equal in both waves of a pair)
+    bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
-    issue(0, 0);  // ntiles >= 1
+    for (int t = 0; t < min(3, ntiles); ++t) issue(t);
 
     for (int t = 0; t < ntiles; ++t) {
-      // wait for this wave's loads of tile t (the only ones in flight)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      // tile t landed for every wave; every wave is done with tile t-1 (its
-      // bf16 stage, the score exchange, and for e4m3 the staging buffer of
-      // tile t+1)
+      // wait for this wave's loads of tile t; those of the (at most two) later
+      // tiles already issued may stay in flight
+      const int later = min(2, ntiles - 1 - t);
+      if (later == 2) {
+        if constexpr (!kFp8) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else if (later == 1) {
+        if constexpr (!kFp8) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts above");
+      // tile t landed for every wave; every wave is done with tile t-1, whose
+      // load stage receives tile t+3
       __syncthreads();
-      if (t + 1 < ntiles) issue(t + 1, (t + 1) % 2);
-      const uint8_t* Z = sZ + (kFp8 ? 0 : (t % 2) * kZStageB);
+      // bf16: tile t+3's loads are spread between the score MFMAs below when
+      // it comes in one piece; e4m3 (five loads a wave) issues them at once
+      const bool spread = !kFp8 && t + 3 < ntiles && one_piece(t + 3);
+      const void* sbn = cache;
+      if (spread) {
+        sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 3) * kDecBN) *
+                                        (kFp8 ? kF8RowB : kZRowB));
+      } else if (t + 3 < ntiles) {
+        issue(t + 3);
+      }
+      const uint32_t nbase = lds0 + kStage0 + ((t + 3) % 4) * kStageB;
+      const uint8_t* Z = sZ + (kFp8 ? 0 : (t % 4) * kZStageB);
       if constexpr (kFp8) {
-        const uint8_t* F = sZ + kZStageB + (t % 2) * kF8StageB;
+        const uint8_t* F = sZ + kStage0 + (t % 4) * kF8StageB;
 #pragma unroll
-        for (int i = 0; i < (kF8Units + kDecThreads - 1) / kDecThreads; ++i) {
+        for (int i = 0; i < kF8Units / kDecThreads; ++i) {
           const int u = tid + kDecThreads * i;  // row u / 72, bf16 chunk u % 72
-          if (u < kF8Units) {
-            const int r = u / kZRowChunks, c = u - r * kZRowChunks;
-            const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
-            *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
-          }
+          const int r = u / kZRowChunks, c = u - r * kZRowChunks;
+          const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
+          *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
         }
         __syncthreads();  // the bf16 tile is complete
       }
       const int kt = kt0 + t * kDecBN;
 
-      // ---- partial S^T over this wave's depth half: 32 keys x 32 heads ----
-      f32x16 s;
+      // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
+      auto scores = [&](auto with_dma) __attribute__((always_inline)) {
+        f32x16 sa, sb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+        for (int i = 0; i < 16; ++i) { sa[i] = 0.f; sb[i] = 0.f; }
+        constexpr int kAhead = 4;
+        constexpr int kEvery = kFp8 ? 8 : 4;  // one load per 4 (e4m3: 8) score steps
+        bf16x8 zb[kAhead];
+        auto zload = [&](int ks) __attribute__((always_inline)) {
+          return *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
+        };
 #pragma unroll
-      for (int ks = 0; ks < kHalfSteps; ++ks) {
-        const bf16x8 za = *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
-        const bf16x8 qa = ks < kQRegSteps ? qf[ks < kQRegSteps ? ks : 0]
-                                          : *(const bf16x8*)(qtab + 32 * (ks - kQRegSteps));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za, qa, s, 0, 0, 0);
-      }
-      // LDS operands run about four MFMAs ahead
-      __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+        for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
 #pragma unroll
-      for (int i = 0; i < kHalfSteps; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
-        if (i < kQRegSteps - 4) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);
-        else if (i < kHalfSteps - 4) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);
-      }
-      // exchange the partial scores with the other wave of the pair (lane l of
-      // both waves holds the same keys and heads)
+        for (int ks = 0; ks < kQSteps; ++ks) {
+          if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sb, 0, 0, 0);
+          else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sa, 0, 0, 0);
+          if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
+          if constexpr (decltype(with_dma)::value) {
+            if (ks % kEvery == 0 && ks / kEvery < kLoadsPerWave) {
+              const int j = ks / kEvery;
+              if (!kFp8 || j < kLoadsPerWave - 1 || wave + kDecWaves * j < kF8Loads)
+                dma16_s_nb(sbn, dma_off(j), nbase + (wave + kDecWaves * j) * 1024);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = s[4 * g + j];
-        *(f32x4*)(xown + g * 1024) = v;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = *(const f32x4*)(xpeer + g * 1024);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s[4 * g + j] += v[j];
-      }
+        for (int i = 0; i < 16; ++i) sa[i] += sb[i];
+        return sa;
+      };
+      f32x16 s = spread ? scores(std::integral_constant<bool, true>())
+                        : scores(std::integral_constant<bool, false>());
 
       // register i holds tile row 16*(i/8) + 8*hf + i%8
       if (kt < k0 || kt + kDecBN > k1) {
@@ -480,22 +474,25 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       }
       l_run += sum_with_lane32(psum);
 
-      // ---- O^T[this wave's 256 dims x 32 heads] += Z^T P^T ----
+      // ---- O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four
+      // MFMAs ahead in rotating registers ----
+      {
+        constexpr int kAhead = 4;
+        bf16x8 vb[kAhead];
+        auto vload = [&](int i) __attribute__((always_inline)) {
+          const int md = i >> 1, ks = i & 1;
+          const bf16x4 a0 = ds_read_tr16(Z + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
+          const bf16x4 a1 = ds_read_tr16(Z + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
+          return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
 #pragma unroll
-      for (int md = 0; md < 8; ++md)
+        for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x4 a0 = ds_read_tr16(Z + tr_base[ks][0][md & 1] + 128 * (md >> 1));
-          const bf16x4 a1 = ds_read_tr16(Z + tr_base[ks][1][md & 1] + 128 * (md >> 1));
-          const bf16x8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
+        for (int i = 0; i < 32; ++i) {
+          o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
+          if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      // transposed reads eight ahead (four MFMAs) of the value product
-      __builtin_amdgcn_sched_group_barrier(0x0100, 8, 1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 1);
-        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x0100, 2, 1);
       }
     }
 
@@ -504,19 +501,19 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     // instruction writes 1 KB in one piece (32 heads x 32 bytes).
     if (hvalid) {
       const size_t base = ((size_t)(w + b) * a.H + head);
-      // O^T register i of block md: dim 256 hd + 32 md + 8 (i / 4) + 4 hf + i % 4
+      // O^T register i of block md: dim 32 md + 8 (i / 4) + 4 hf + i % 4
       float* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
 #pragma unroll
-      for (int md = 0; md < 8; ++md)
+      for (int md = 0; md < 16; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
-          *(f32x4*)(op + (size_t)(32 * hd + 4 * md + g) * a.H * 8) = v;
+          *(f32x4*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
         }
-      if (hd == 0 && hf == 0) {
-        // a pair whose scores outgrew the reference hands (exact maximum, -1)
+      if (hf == 0) {
+        // a wave whose scores outgrew the reference hands (exact maximum, -1)
         // to the combine step, which recomputes this partial against it
         a.part_ml[base * 2 + 0] = halted ? m_seen : m_ref;
         a.part_ml[base * 2 + 1] = halted ? -1.0f : l_run;
