@@ -123,8 +123,10 @@ __global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* _
 // 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
 // the score reads (16 rows at one column) and the transposed reads (4 rows x
 // 64 bytes) touch distinct LDS banks. An e4m3 tile lands, rows as stored, in
-// one of four staging buffers and is widened exactly into the single bf16
-// stage before use.
+// one of four staging buffers; once the value product of the tile before it
+// is issued, every wave widens exactly the bytes its own loads brought into
+// the other of two bf16 stages, so the one barrier per tile also publishes
+// the widened tile.
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBN = 32;                          // keys per tile
@@ -143,11 +145,9 @@ constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
 constexpr int kF8Stages = 4;
 constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
 constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 5 (waves 2, 3: 4)
-constexpr int kF8Units = kDecBN * kZRowChunks;      // 2304 groups of 8 codes per tile
 static_assert(kZLoads % kDecWaves == 0, "even bf16 loads per wave");
 static_assert(kF8Loads == 4 * kDecWaves + 2, "e4m3: waves 0, 1 load five times, waves 2, 3 four");
-static_assert(kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
-static_assert(kF8Units % kDecThreads == 0, "even widening per thread");
+static_assert(2 * kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
 static_assert(kPTWindow % kDecThreads == 0, "even page-table staging per thread");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
@@ -204,12 +204,12 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
-  // bf16: four stages; e4m3: one bf16 stage and four staging buffers behind it
+  // bf16: four stages; e4m3: two bf16 stages and four staging buffers behind them
   __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
   __shared__ int sPT[kPTWindow];
   constexpr int kLoadsPerWave = kFp8 ? kF8LoadsPerWave : kZLoadsPerWave;
   constexpr int kStageB = kFp8 ? kF8StageB : kZStageB;
-  constexpr int kStage0 = kFp8 ? kZStageB : 0;        // byte offset of load stage 0
+  constexpr int kStage0 = kFp8 ? 2 * kZStageB : 0;    // byte offset of load stage 0
 
   const int w = blockIdx.x;
   if (w >= a.G) return;
@@ -362,25 +362,51 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
     for (int t = 0; t < min(3, ntiles); ++t) issue(t);
-
-    for (int t = 0; t < ntiles; ++t) {
-      // wait for this wave's loads of tile t; those of the (at most two) later
-      // tiles already issued may stay in flight
-      const int later = min(2, ntiles - 1 - t);
+    // e4m3: each wave waits for its own loads of tile tt and widens exactly
+    // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
+    // one row) into bf16 stage tt % 2; the barrier at the top of the tile
+    // loop then publishes the whole tile. later: tiles issued after tt whose
+    // loads may stay in flight.
+    auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
       if (later == 2) {
-        if constexpr (!kFp8) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+        if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       } else if (later == 1) {
-        if constexpr (!kFp8) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts above");
-      // tile t landed for every wave; every wave is done with tile t-1, whose
-      // load stage receives tile t+3
+      const uint8_t* F = sZ + kStage0 + (tt % 4) * kF8StageB;
+      uint8_t* D = sZ + (tt % 2) * kZStageB;
+#pragma unroll
+      for (int j = 0; j < kF8LoadsPerWave; ++j) {
+        const int p = wave + kDecWaves * j;
+        if (p < kF8Loads) {
+          const int byte = p * 1024 + lane * 16;
+          const int r = byte / kF8RowB;
+          const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
+          const u32x4 v = *(const u32x4*)(F + byte);
+          *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
+          *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
+        }
+      }
+    };
+    if constexpr (kFp8) widen_own(0, min(2, ntiles - 1));
+
+    for (int t = 0; t < ntiles; ++t) {
+      // wait for this wave's loads of tile t; those of the (at most two) later
+      // tiles already issued may stay in flight
+      if constexpr (!kFp8) {
+        const int later = min(2, ntiles - 1 - t);
+        if (later == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
+      // tile t is in place for every wave (bf16: landed; e4m3: widened); every
+      // wave is done with tile t-1, whose stage receives tile t+3 (e4m3: its
+      // bf16 stage receives tile t+1 at the end of this iteration)
       __syncthreads();
       // bf16: tile t+3's loads are spread between the score MFMAs below when
       // it comes in one piece; e4m3 (five loads a wave) issues them at once
@@ -393,18 +419,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         issue(t + 3);
       }
       const uint32_t nbase = lds0 + kStage0 + ((t + 3) % 4) * kStageB;
-      const uint8_t* Z = sZ + (kFp8 ? 0 : (t % 4) * kZStageB);
-      if constexpr (kFp8) {
-        const uint8_t* F = sZ + kStage0 + (t % 4) * kF8StageB;
-#pragma unroll
-        for (int i = 0; i < kF8Units / kDecThreads; ++i) {
-          const int u = tid + kDecThreads * i;  // row u / 72, bf16 chunk u % 72
-          const int r = u / kZRowChunks, c = u - r * kZRowChunks;
-          const u32x2 v = *(const u32x2*)(F + r * kF8RowB + c * 8);
-          *(u32x4*)(sZ + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(v);
-        }
-        __syncthreads();  // the bf16 tile is complete
-      }
+      const uint8_t* Z = sZ + (kFp8 ? (t % 2) : (t % 4)) * kZStageB;
       const int kt = kt0 + t * kDecBN;
 
       // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
@@ -494,6 +509,8 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      if constexpr (kFp8)
+        if (t + 1 < ntiles) widen_own(t + 1, min(2, ntiles - 2 - t));
     }
 
     // partial state of (w, b): slot w + b. The output is stored by groups of
