@@ -26,6 +26,10 @@
  *   the host, so a sequence of calls can be captured into a HIP graph.
  *   Device-resident plan values (buffer_lengths) are read on the device.
  * - All tensors are dense, row-major and contiguous in the shapes given.
+ *   Tensor pointers (activations, caches, weights, outputs, workspaces; not
+ *   the small per-sequence offset, length and page-table arrays) must be
+ *   16-byte aligned, as device allocations are; a misaligned one is
+ *   MLA_ERR_INVALID_ARG.
  *   "bf16" is bfloat16, "e4m3" is OCP float8_e4m3fn (1-4-3, bias 7, no
  *   infinities), each passed as raw storage.
  * - Every function returns MLA_OK (0) or a negative status. Host-checkable
@@ -146,7 +150,9 @@ int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
  * ("mla_prefill_decode_graph_bf16" page, Args "w_k" and "w_uv"):
  *   K_nope[r, h, d] = sum_l w_k[h*128 + d, l] latent[r, l]
  *   V[r, h, d]      = sum_l w_uv[h, d, l]     latent[r, l]
- * for r < *buffer_length_c; bf16 MFMA with fp32 accumulation.
+ * for r < *buffer_length_c; bf16 MFMA with fp32 accumulation. Rows from
+ * *buffer_length_c up to the next multiple of 64 are written as zeros (the
+ * attention's last key tile of a chunk reads them, masked).
  *
  * Output layouts are the ones the attention kernel streams:
  *   k_nope_out  [num_heads, max_rows, 128], bf16 or e4m3 (k_dtype)

@@ -1,5 +1,6 @@
 // C ABI of libmla.so: host-side validation, workspace layout and kernel
 // launches. Declarations and contracts are in include/mla.h.
+#include <initializer_list>
 #include <math.h>
 #include <stdio.h>
 #include <string.h>
@@ -32,6 +33,13 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool dtype_ok(int32_t d) { return d == MLA_BF16 || d == MLA_FP8_E4M3FN; }
+
+// the kernels move tensor data in 16-byte vectors and direct-to-LDS loads
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 15) return true;
+  return false;
+}
 size_t dsize(int32_t d) { return d == MLA_FP8_E4M3FN ? 1 : 2; }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -197,6 +205,8 @@ int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
   if (!latent_out || !krope_out || !kv_cache || !page_table || !buffer_row_offsets_c ||
       !cache_offsets_c || !buffer_length_c || !kv_norm_gamma || !freqs_cis)
     return fail(MLA_ERR_INVALID_ARG, "mla_gather_norm_rope: null pointer");
+  if (misaligned({latent_out, krope_out, kv_cache, kv_norm_gamma, freqs_cis}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_gather_norm_rope: tensor not 16-byte aligned");
   if (!dtype_ok(krope_dtype) || !dtype_ok(cache_dtype))
     return fail(MLA_ERR_UNSUPPORTED, "mla_gather_norm_rope: dtype");
   if (batch_size < 1 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
@@ -229,6 +239,8 @@ int mla_up_project(void* k_nope_out, void* v_t_out, int32_t k_dtype, const void*
                    int32_t num_heads, int32_t max_rows, hipStream_t stream) {
   if (!k_nope_out || !v_t_out || !latent || !w_k || !w_uv || !buffer_length_c)
     return fail(MLA_ERR_INVALID_ARG, "mla_up_project: null pointer");
+  if (misaligned({k_nope_out, v_t_out, latent, w_k, w_uv}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_up_project: tensor not 16-byte aligned");
   if (!dtype_ok(k_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_up_project: dtype");
   if (num_heads < 1 || num_heads > 1024 || max_rows < 64 || max_rows % 64 != 0)
     return fail(MLA_ERR_INVALID_ARG, "mla_up_project: num_heads=%d max_rows=%d", num_heads,
@@ -291,6 +303,8 @@ int mla_prefill_attention(void* output, const void* q, int32_t dtype, const void
   if (!output || !q || !k_nope || !v_t || !krope || !input_row_offsets || !cache_lengths ||
       !buffer_row_offsets_c || !cache_offsets_c || !buffer_length_c)
     return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: null pointer");
+  if (misaligned({output, q, k_nope, v_t, krope, workspace}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: tensor not 16-byte aligned");
   if (!dtype_ok(dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill_attention: dtype");
   if (batch_size < 1 || total_q < 1 || num_heads < 1 || num_heads > 1024 || max_rows < 64 ||
       max_rows % 64 != 0 || max_prompt_len < 1 || !(scale > 0.f))
@@ -332,6 +346,8 @@ int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* inpu
       !buffer_row_offsets || !cache_offsets || !buffer_lengths || !w_k || !w_uv ||
       !kv_norm_gamma || !freqs_cis)
     return fail(MLA_ERR_INVALID_ARG, "mla_prefill: null pointer");
+  if (misaligned({output, q, kv_cache, w_k, w_uv, kv_norm_gamma, freqs_cis, workspace}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_prefill: tensor not 16-byte aligned");
   if (!dtype_ok(dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_prefill: dtype");
   if (batch_size < 1 || total_q < 1 || num_heads < 1 || num_heads > 1024 || max_chunks < 1 ||
       max_rows < 1 || max_prompt_len < 1 || page_size < 1 || max_pages_per_seq < 1 ||
@@ -388,6 +404,8 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                size_t workspace_bytes, hipStream_t stream) {
   if (!output || !q || !context_lengths || !kv_cache || !page_table || !w_uk || !w_uv)
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer");
+  if (misaligned({output, q, kv_cache, w_uk, w_uv, workspace}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode: tensor not 16-byte aligned");
   if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_decode: dtype");
   if (batch_size < 1 || num_heads < 1 || num_heads > 128 || page_size < 1 ||
       max_pages_per_seq < 1 || num_pages < 1 || max_context_len < 1 || num_partitions < 0 ||

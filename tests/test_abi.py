@@ -49,6 +49,12 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.mla_prefill_plan(fake, fake, fake, None, fake, fake, 4096, 1, 1 << 20, None) == -1
     # unsupported dtype
     assert lib.mla_up_project(fake, fake, 7, fake, fake, fake, fake, 2, 128, None) == -2
+    # a tensor pointer that is not 16-byte aligned
+    odd = P(0x1008)
+    assert lib.mla_up_project(fake, odd, 0, fake, fake, fake, fake, 2, 128, None) == -1
+    assert b"aligned" in lib.mla_last_error()
+    assert lib.mla_decode(fake, fake, fake, odd, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
+                          0.1, fake, 1 << 40, None) == -1
     # max_rows not a multiple of 64
     assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
     # workspace too small

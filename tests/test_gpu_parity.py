@@ -161,6 +161,10 @@ def test_up_project(B, H, R, n):
     scale_k = np.sqrt((lat ** 2) @ (oracle.bf16_to_f64(wk_bits) ** 2).T).reshape(n, H, 128)
     assert (np.abs(gk - rk) <= 2.0 ** -8 * np.abs(rk) + 1e-5 * scale_k + 1e-6).all()
     assert (np.abs(gv - rv) <= 2.0 ** -8 * np.abs(rv) + 1e-5 * np.abs(rv).max() + 1e-5).all()
+    # rows past the chunk up to the next 64-row tile are zeros: a key tile that
+    # runs past the chunk reads finite values
+    n64 = min(-(-n // 64) * 64, R)
+    assert (_f64(kn)[:, n:n64] == 0).all() and (_f64(vt)[:, :, n:n64] == 0).all()
 
 
 # ---------------------------------------------------------------------------
