@@ -4,23 +4,90 @@
 //
 // Four steps:
 //  1. absorb:   q_abs[b, h] = [w_uk[h] q_nope[b, h] | q_rope[b, h]] (576 wide),
-//               bf16 MFMA, one wave per 32x32 output tile, operands read
-//               straight from global memory (both are contiguous along the
-//               128-long reduction).
+//               bf16 MFMA, operands read straight from global memory (both
+//               are contiguous along the 128-long reduction).
 //  2. split-KV: the batch's contexts laid end to end are cut into G equal key
 //               ranges; one workgroup per range streams its 576-wide cache
 //               rows once for all 128 heads and keeps an unnormalised
 //               softmax state (max, sum, O_lat) per sequence it touches.
 //  3. combine:  per (sequence, head), the states of the key ranges that
 //               touched the sequence are merged by log-sum-exp into o_lat.
-//  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA like the absorb.
+//  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA, the 512-long
+//               reduction split over the waves of a workgroup.
 #include "kernels.hpp"
 
 namespace mla {
 
 // ---------------------------------------------------------------------------
-// 1, 4. per-head small GEMMs: C[b, n] = sum_k X[b, k] W[n, k]
+// 1, 4. per-head small GEMMs (bf16 MFMA 32x32x16, fp32 accumulation)
 // ---------------------------------------------------------------------------
+// Both are latency-bound (about 1 GFLOP and 17 MB of weights each at 64
+// sequences and 128 heads): every wave issues all of its operand loads
+// straight from global memory at once (both operands are contiguous along
+// the reduction), then runs its MFMAs. A lane's 16-byte operand fragment is
+// row l32 of a 32-row block, reduction elements 16 k + 8 hf .. + 7.
+
+// q_abs[b, h, 0:512] = w_uk[h] q_nope[b, h]; q_abs[b, h, 512:576] = q_rope[b, h].
+// Grid (512 / 128, H, ceil(B / 64)); wave v computes latent dims
+// 128 blockIdx.x + 32 v .. + 31 for 64 sequences (two 32-row blocks). The
+// workgroups of column block 0 also copy the rope part of their sequences.
+__global__ void __launch_bounds__(256) absorb_kernel(uint16_t* __restrict__ q_abs,
+                                                     const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ w_uk, int B,
+                                                     int H) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int h = blockIdx.y;
+  const int n0 = blockIdx.x * 128 + wave * 32;
+  const int b0 = blockIdx.z * 64;
+  constexpr int kSteps = kNope / 16;  // 8
+  const uint16_t* wp = w_uk + ((size_t)h * kLora + n0 + l32) * kNope + hf * 8;
+  u32x4 wf[kSteps], xf[2][kSteps];
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) wf[k] = *(const u32x4*)(wp + 16 * k);
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    const int brow = b0 + 32 * bt + l32;
+    const uint16_t* xp = q + ((size_t)min(brow, B - 1) * H + h) * kQDepth + hf * 8;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) {
+      xf[bt][k] = *(const u32x4*)(xp + 16 * k);
+      if (brow >= B) xf[bt][k] = u32x4{0, 0, 0, 0};
+    }
+  }
+  f32x16 acc[2];
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[bt][i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k)
+      acc[bt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xf[bt][k]),
+                                                        __builtin_bit_cast(bf16x8, wf[k]), acc[bt],
+                                                        0, 0, 0);
+  }
+  // lane holds latent dim n0 + l32 of rows b0 + 32 bt + 8 (i / 4) + 4 hf + i % 4
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int b = b0 + 32 * bt + (i >> 2) * 8 + hf * 4 + (i & 3);
+      if (b < B) q_abs[((size_t)b * H + h) * kCache + n0 + l32] = (uint16_t)f32_to_bf16_rne(acc[bt][i]);
+    }
+  if (blockIdx.x == 0) {
+    // 64 sequences x 64 rope values: 512 pieces of 16 bytes
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int piece = it * 256 + tid;
+      const int b = b0 + (piece >> 3), c = (piece & 7) * 8;
+      if (b < B)
+        *(u32x4*)(q_abs + ((size_t)b * H + h) * kCache + kLora + c) =
+            *(const u32x4*)(q + ((size_t)b * H + h) * kQDepth + kNope + c);
+    }
+  }
+}
+
+// Projection: C[b, n] = sum_k X[b, k] W[n, k] per head.
 // X rows: x + b*x_stride (K contiguous, bf16); W rows: w + n*K (K contiguous).
 // Output: y[b*y_stride + n] as bf16. One wave computes a 32 (b) x 32 (n) tile;
 // K is a multiple of 16. kTwoTerm: X = hi + lo, with lo stored K elements
@@ -70,16 +137,6 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
       y[o] = (uint16_t)f32_to_bf16_rne(acc[i]);
     }
   }
-}
-
-// copy q_rope into the last 64 columns of q_abs
-__global__ void copy_rope_kernel(uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q,
-                                 int B, int H) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*H*64
-  if (i >= (long)B * H * kRope) return;
-  const long bh = i / kRope;
-  const int e = (int)(i - bh * kRope);
-  q_abs[bh * kCache + kLora + e] = q[bh * kQDepth + kNope + e];
 }
 
 // ---------------------------------------------------------------------------
@@ -666,31 +723,50 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
   if (span.y >= span.x) {
+    // the maximum over the partials: lanes stride over the ranges
     float M = -INFINITY;
-    for (int w = span.x; w <= span.y; ++w) {
-      if (c.wstart[w] >= c.wstart[w + 1]) continue;  // empty range: no partial
-      M = fmaxf(M, c.part_ml[((size_t)(w + b) * c.H + h) * 2]);
+    for (int w0 = span.x; w0 <= span.y; w0 += 64) {
+      const int w = w0 + lane;
+      if (w <= span.y && c.wstart[w] < c.wstart[w + 1])  // empty range: no partial
+        M = fmaxf(M, c.part_ml[((size_t)(w + b) * c.H + h) * 2]);
     }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    // the weighted sum, four ranges' states and outputs loaded together
     float L = 0.f;
-    for (int w = span.x; w <= span.y; ++w) {
-      if (c.wstart[w] >= c.wstart[w + 1]) continue;
-      const size_t base = (size_t)(w + b) * c.H + h;
-      const float m = c.part_ml[base * 2];
-      float l = c.part_ml[base * 2 + 1];
-      float ow[8];
-      if (l < 0.f) {  // marked partial: recompute (wave-uniform)
-        recompute_partial(c, w, b, h, m, ow, l);
-      } else {
+    for (int w0 = span.x; w0 <= span.y; w0 += 4) {
+      bool ok[4];
+      float m[4], l[4];
+      f32x4 v0[4], v1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = w0 + j;
+        ok[j] = w <= span.y && c.wstart[w] < c.wstart[w + 1];
+        const size_t base = (size_t)(w + b) * c.H + h;
         const float* po = c.part_o + (((size_t)(w + b) * (kLora / 8) + lane) * c.H + h) * 8;
-        const f32x4 v0 = *(const f32x4*)(po);
-        const f32x4 v1 = *(const f32x4*)(po + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { ow[j] = v0[j]; ow[4 + j] = v1[j]; }
+        if (ok[j]) {
+          m[j] = c.part_ml[base * 2];
+          l[j] = c.part_ml[base * 2 + 1];
+          v0[j] = *(const f32x4*)(po);
+          v1[j] = *(const f32x4*)(po + 4);
+        }
       }
-      const float wt = __builtin_amdgcn_exp2f(m - M);
-      L += wt * l;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wt, ow[j], acc[j]);
+      for (int j = 0; j < 4; ++j) {
+        if (!ok[j]) continue;
+        float ow[8];
+        float lj = l[j];
+        if (lj < 0.f) {  // marked partial: recompute (wave-uniform)
+          recompute_partial(c, w0 + j, b, h, m[j], ow, lj);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { ow[e] = v0[j][e]; ow[4 + e] = v1[j][e]; }
+        }
+        const float wt = __builtin_amdgcn_exp2f(m[j] - M);
+        L += wt * lj;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt, ow[e], acc[e]);
+      }
     }
     const float inv = 1.f / L;
 #pragma unroll
@@ -712,16 +788,8 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
 // ---------------------------------------------------------------------------
 hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16_t* w_uk, int B,
                                 int H, hipStream_t stream) {
-  // q_lat[b, h, l] = sum_d q[b, h, d] w_uk[h, l, d]: X = q (stride 192 per h),
-  // W = w_uk[h] rows (l), K = 128, N = 512
-  const int ntn = kLora / 32;
-  const int tiles = ((B + 31) / 32) * ntn;
-  const dim3 grid((tiles + 3) / 4, H);
-  hipLaunchKernelGGL((head_gemm_kernel<kNope>), grid, dim3(256), 0, stream, q_abs, q, w_uk,
-                     B, kLora, (long)H * kQDepth, (long)kQDepth, (long)kLora * kNope,
-                     (long)H * kCache, (long)kCache, ntn);
-  const long n = (long)B * H * kRope;
-  hipLaunchKernelGGL(copy_rope_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, q_abs, q, B, H);
+  const dim3 grid(kLora / 128, H, (B + 63) / 64);
+  hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), 0, stream, q_abs, q, w_uk, B, H);
   return hipGetLastError();
 }
 
