@@ -165,6 +165,44 @@ def norm_rope_rows(raw: np.ndarray, positions: np.ndarray, gamma: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# KV write path (mla_prefill_decode_graph_bf16 page: Parameters "kv_input_fn",
+# the new tokens' raw latent [tot_seq_len, 576]; Args "kv_norm_gamma",
+# "epsilon", "freqs_cis", "input_row_offsets" and the paged KV cache)
+# ---------------------------------------------------------------------------
+
+
+def kv_write(pool: np.ndarray, page_table: np.ndarray, kv_input: np.ndarray,
+             input_row_offsets, cache_lengths, gamma: np.ndarray, freqs: np.ndarray,
+             eps: float, page_size: int, lora: int = 512) -> np.ndarray:
+    """The pool (values, any float dtype) after storing every new token's row,
+    normalised and rotated: token i of sequence b (row input_row_offsets[b] + i
+    of kv_input) sits at position cache_lengths[b] + i; its stored row is the
+    RMSNorm'd latent (times gamma) followed by the rope part rotated for that
+    position, in the slot the page table gives the position. Tokens whose
+    logical page is outside the page table, whose page id is outside the pool,
+    or whose position is outside freqs are not written. The reading: this is
+    the processed-cache convention decode reads (rows as stored)."""
+    out = np.array(pool, dtype=np.float64, copy=True)
+    flat = out.reshape(-1, out.shape[-1])
+    num_pages = pool.shape[0]
+    off = np.asarray(input_row_offsets, dtype=np.int64)
+    clen = np.asarray(cache_lengths, dtype=np.int64)
+    for b in range(len(clen)):
+        rows = np.asarray(kv_input[off[b]:off[b + 1]], dtype=np.float64)
+        pos = clen[b] + np.arange(rows.shape[0], dtype=np.int64)
+        lp = pos // page_size
+        ok = (lp < page_table.shape[1]) & (pos < freqs.shape[0])
+        pg = np.where(ok, page_table[b, np.minimum(lp, page_table.shape[1] - 1)], -1)
+        ok &= (pg >= 0) & (pg < num_pages)
+        if not ok.any():
+            continue
+        latn, kr = norm_rope_rows(rows[ok], pos[ok], gamma, freqs, eps, lora)
+        flat[pg[ok].astype(np.int64) * page_size + pos[ok] % page_size] = \
+            np.concatenate([latn, kr], axis=1)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Up-projection (mla_prefill_decode_graph_bf16 page: Args "w_k", "w_uv")
 # ---------------------------------------------------------------------------
 

@@ -382,3 +382,59 @@ def test_decode_matches_torch_sdpa_single_kv_head():
             ref = torch.nn.functional.scaled_dot_product_attention(
                 q, torch.from_numpy(K)[None], torch.from_numpy(V)[None], scale=wl.scale)
             assert np.allclose(out[b, h], ref[0, 0].numpy(), rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# KV write path: every new token lands in exactly the slot of its position
+# ---------------------------------------------------------------------------
+
+def test_kv_write_places_each_token_and_touches_nothing_else():
+    rng = np.random.default_rng(11)
+    ps, num_pages, maxp = 4, 16, 5
+    cached = [3, 0, 9]
+    new = [6, 2, 0]
+    off = np.concatenate([[0], np.cumsum(new)])
+    pt = rng.permutation(num_pages)[:3 * maxp].reshape(3, maxp).astype(np.int32)
+    pt[0, 2] = -1                      # the page of sequence 0's last token is missing
+    pool = rng.standard_normal((num_pages, ps, 576))
+    x = rng.standard_normal((int(off[-1]), 576))
+    freqs = np.zeros((64, 64))
+    freqs[:, 0::2] = 1.0               # identity rotation
+    out = oracle.kv_write(pool, pt, x, off, cached, np.ones(512), freqs, 0.0, ps)
+    expect = pool.copy()
+    written = set()
+    for b in range(3):                 # one token at a time, by hand
+        for i in range(new[b]):
+            p = cached[b] + i
+            page = int(pt[b, p // ps])
+            if page < 0:
+                continue
+            row = x[off[b] + i]
+            lat = row[:512] / math.sqrt(sum(v * v for v in row[:512]) / 512)
+            expect[page, p % ps] = np.concatenate([lat, row[512:]])
+            written.add((page, p % ps))
+    assert len(written) == 7           # 5 of 6 (one page missing) + 2 + 0 tokens
+    assert np.allclose(out, expect, rtol=1e-12, atol=0)
+    for pg in range(num_pages):
+        for sl in range(ps):
+            if (pg, sl) not in written:
+                assert np.array_equal(out[pg, sl], pool[pg, sl])
+
+
+def test_kv_write_rotates_by_the_position_angle():
+    # one token at position 5: rope part (1, 0) pairs rotate to (cos, sin) of
+    # that position's angles; a unit-rms latent with gamma 2 doubles
+    ps = 8
+    pt = np.array([[0]], dtype=np.int32)
+    pool = np.zeros((1, ps, 576))
+    x = np.zeros((1, 576))
+    x[0, :512] = 1.0
+    x[0, 512::2] = 1.0
+    ang = np.outer(np.arange(8), np.arange(32) * 0.1)
+    freqs = np.zeros((8, 64))
+    freqs[:, 0::2], freqs[:, 1::2] = np.cos(ang), np.sin(ang)
+    out = oracle.kv_write(pool, pt, x, [0, 1], [5], np.full(512, 2.0), freqs, 0.0, ps)
+    assert np.allclose(out[0, 5, :512], 2.0, rtol=1e-15)
+    assert np.allclose(out[0, 5, 512::2], np.cos(ang[5]), atol=1e-15)
+    assert np.allclose(out[0, 5, 513::2], np.sin(ang[5]), atol=1e-15)
+    assert np.array_equal(out[0, :5], pool[0, :5]) and np.array_equal(out[0, 6:], pool[0, 6:])
