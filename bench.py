@@ -11,7 +11,8 @@ per-call durations; the attention call is the dominant kernel.
 
 A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
 batch (contexts U{4096..32768}), with a bf16 and then an e4m3 cache, and
-reports achieved HBM bandwidth.
+reports achieved HBM bandwidth. A third times mla_kv_write storing the
+prompt's 4096 new tokens into the paged cache (normalised, rotated).
 
 Before the W warm-up steps, about S seconds (default 1) of the same work run
 untimed, so that the GPU clock has left its idle state; the K timed steps are
@@ -196,6 +197,49 @@ def bench_decode(args, binding, torch, recipe="decode_b64"):
     return dict(ms=ms, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows)
 
 
+def bench_kv_write(args, binding, torch):
+    """mla_kv_write on the prompt of dsv3_prefill_4k: 4096 new tokens' raw
+    576-wide rows normalised, rotated and stored in a bf16 pool of 128-row
+    pages (shuffled page table). A launch takes microseconds, so calls are
+    timed in groups of 20 between events."""
+    import numpy as np
+    from workloads import f32_to_bf16_bits
+    from workloads.gen import rope_table_bits
+
+    rng = np.random.default_rng(9)
+    n, ps = 4096, 128
+    pages = n // ps
+    num_pages = pages + 8
+    pt = torch.from_numpy(rng.permutation(num_pages)[:pages].reshape(1, pages).astype(np.int32)).cuda()
+    bf = lambda a: torch.from_numpy(f32_to_bf16_bits(a.astype(np.float32)).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    x = bf(rng.standard_normal((n, 576)))
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(512))
+    freqs = torch.from_numpy(rope_table_bits(n, 64).view(np.int16)).view(torch.bfloat16).cuda()
+    cache = torch.zeros((num_pages, ps, 576), dtype=torch.bfloat16, device="cuda")
+    offs = torch.tensor([0, n], dtype=torch.uint32, device="cuda")
+    clen = torch.tensor([0], dtype=torch.uint32, device="cuda")
+
+    def call():
+        binding.mla_kv_write(cache, pt, x, offs, clen, gamma, freqs, 1e-6)
+
+    warm_clock(call, args.warm_seconds / 4, torch)
+    group = 20
+    evs = []
+    for _ in range(max(1, args.steps // 4)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(group):
+            call()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / (len(evs) * group)
+    bytes_alg = n * (576 * 2 + 576 * 2 + 64 * 2) + 512 * 2
+    return dict(ms=ms, bytes=bytes_alg)
+
+
 def cpu_baseline(full_wl, heads: int):
     """The oracle as it stands on `heads` of the 128 heads of the same prefill
     workload; returns (attention TFLOP/s on the sample, seconds, threads)."""
@@ -320,6 +364,16 @@ def main():
             "split_kernel_traffic": load_traffic("decode.hip",
                                                  "decode_split_decode_b64_fp8_counters.json"),
         }
+    kw = bench_kv_write(args, binding, torch)
+    gbps = kw["bytes"] / (kw["ms"] * 1e-3) / 1e9
+    line["kv_write"] = {
+        "workload": "mla_kv_write: the 4096 new tokens of dsv3_prefill_4k, raw 576-wide rows "
+                    "normalised, rotated and stored into a bf16 pool of 128-row pages",
+        "ms": round(kw["ms"], 5),
+        "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes": kw["bytes"],
+    }
     if not args.no_cpu:
         tf, sec, threads = cpu_baseline(p["wl"], args.cpu_heads)
         line["cpu_baseline"] = {

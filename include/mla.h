@@ -146,6 +146,39 @@ int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
                          float epsilon, hipStream_t stream);
 
 /*
+ * mla_kv_write -- store the new tokens' latent rows in the paged cache,
+ * normalised and rotated ("mla_prefill_decode_graph_bf16" page: Parameters
+ * "kv_input_fn", the new tokens' raw latent [tot_seq_len, 576]; Args
+ * "kv_norm_gamma", "epsilon", "freqs_cis", "input_row_offsets" and the paged
+ * KV cache). This is the state decode reads: rows as stored.
+ *
+ * Token t of sequence b (input_row_offsets[b] <= t < input_row_offsets[b+1])
+ * sits at position p = cache_lengths[b] + (t - input_row_offsets[b]); with
+ * x = kv_input[t, 0:512], y = kv_input[t, 512:576], F = freqs_cis[p, :]:
+ *   kv_cache[page_table[b, p / page_size], p % page_size, l]       = x_l * gamma_l / sqrt(mean(x^2) + epsilon)
+ *   kv_cache[page_table[b, p / page_size], p % page_size, 512 + 2i] = y_2i F_2i - y_2i+1 F_2i+1
+ *   kv_cache[...,                                          512 + 2i+1] = y_2i F_2i+1 + y_2i+1 F_2i
+ * Arithmetic is fp32; the stored values are rounded to bf16, or to e4m3
+ * (nearest even, saturating at 448) when cache_dtype is MLA_FP8_E4M3FN.
+ *
+ *   kv_cache      bf16 or e4m3 [num_pages, page_size, 576] (device, written)
+ *   page_table    int32 [batch_size, max_pages_per_seq]
+ *   kv_input      bf16 [total_tokens, 576]
+ *   input_row_offsets uint32 [batch_size + 1]; cache_lengths uint32 [batch_size]
+ *   kv_norm_gamma bf16 [512];  freqs_cis bf16 [max_seq_len, 64]
+ * Only the new tokens' slots are written. Tokens whose logical page is past
+ * max_pages_per_seq, whose page id is outside [0, num_pages) or whose position
+ * is not below max_seq_len are skipped. Two tokens mapping to one slot (a
+ * page table that repeats a page) race.
+ */
+int mla_kv_write(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                 const void* kv_input, const uint32_t* input_row_offsets,
+                 const uint32_t* cache_lengths, const void* kv_norm_gamma, const void* freqs_cis,
+                 int32_t batch_size, int32_t total_tokens, int32_t page_size,
+                 int32_t max_pages_per_seq, int32_t num_pages, int32_t max_seq_len, float epsilon,
+                 hipStream_t stream);
+
+/*
  * mla_up_project -- K_nope and V from the normalised latent
  * ("mla_prefill_decode_graph_bf16" page, Args "w_k" and "w_uv"):
  *   K_nope[r, h, d] = sum_l w_k[h*128 + d, l] latent[r, l]

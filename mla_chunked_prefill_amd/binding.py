@@ -33,6 +33,7 @@ _SIGNATURES = {
     "mla_prefill_plan": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _U, _P]),
     "mla_gather_norm_rope": (_I, [_P, _P, _I, _P, _I, _P, _P, _P, _P, _P, _P,
                                   _I, _I, _I, _I, _I, _I, _F, _P]),
+    "mla_kv_write": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P]),
     "mla_up_project": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "mla_prefill_attention_workspace_size": (_S, [_I, _I, _I]),
     "mla_prefill_attention": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -158,6 +159,27 @@ def mla_gather_norm_rope(latent_out, krope_out, kv_cache, page_table, buffer_row
         B, kv_cache.shape[1], page_table.shape[1], kv_cache.shape[0], R, freqs_cis.shape[0],
         float(epsilon), _stream(stream))
     _check("mla_gather_norm_rope", st)
+
+
+def mla_kv_write(kv_cache, page_table, kv_input, input_row_offsets, cache_lengths,
+                 kv_norm_gamma, freqs_cis, epsilon: float, stream=None):
+    B = cache_lengths.shape[0]
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != CACHE:
+        raise ValueError("kv_cache shape")
+    _expect(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table shape")
+    _expect(kv_input, torch.bfloat16, (kv_input.shape[0], CACHE), "kv_input")
+    _expect(input_row_offsets, torch.uint32, (B + 1,), "input_row_offsets")
+    _expect(cache_lengths, torch.uint32, (B,), "cache_lengths")
+    _expect(kv_norm_gamma, torch.bfloat16, (LORA,), "kv_norm_gamma")
+    _expect(freqs_cis, torch.bfloat16, (freqs_cis.shape[0], ROPE), "freqs_cis")
+    st = load().mla_kv_write(
+        _ptr(kv_cache), _dtype_code(kv_cache), _ptr(page_table), _ptr(kv_input),
+        _ptr(input_row_offsets), _ptr(cache_lengths), _ptr(kv_norm_gamma), _ptr(freqs_cis),
+        B, kv_input.shape[0], kv_cache.shape[1], page_table.shape[1], kv_cache.shape[0],
+        freqs_cis.shape[0], float(epsilon), _stream(stream))
+    _check("mla_kv_write", st)
 
 
 def mla_up_project(k_nope_out, v_t_out, latent, w_k, w_uv, buffer_length_c, stream=None):

@@ -234,6 +234,41 @@ int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
                     "gather kernel");
 }
 
+int mla_kv_write(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                 const void* kv_input, const uint32_t* input_row_offsets,
+                 const uint32_t* cache_lengths, const void* kv_norm_gamma, const void* freqs_cis,
+                 int32_t batch_size, int32_t total_tokens, int32_t page_size,
+                 int32_t max_pages_per_seq, int32_t num_pages, int32_t max_seq_len, float epsilon,
+                 hipStream_t stream) {
+  if (!kv_cache || !page_table || !kv_input || !input_row_offsets || !cache_lengths ||
+      !kv_norm_gamma || !freqs_cis)
+    return fail(MLA_ERR_INVALID_ARG, "mla_kv_write: null pointer");
+  if (misaligned({kv_cache, kv_input, kv_norm_gamma, freqs_cis}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_kv_write: tensor not 16-byte aligned");
+  if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_kv_write: dtype");
+  if (batch_size < 1 || total_tokens < 0 || page_size < 1 || max_pages_per_seq < 1 ||
+      num_pages < 1 || max_seq_len < 1 || !(epsilon >= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_kv_write: sizes");
+  if (total_tokens == 0) return MLA_OK;
+  mla::KvWriteArgs a;
+  a.cache = kv_cache;
+  a.page_table = page_table;
+  a.input = (const uint16_t*)kv_input;
+  a.offs = input_row_offsets;
+  a.clen = cache_lengths;
+  a.gamma = (const uint16_t*)kv_norm_gamma;
+  a.freqs = (const uint16_t*)freqs_cis;
+  a.B = batch_size;
+  a.total = total_tokens;
+  a.ps = page_size;
+  a.maxp = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.max_seq_len = max_seq_len;
+  a.eps = epsilon;
+  return hip_status(mla::launch_kv_write(a, cache_dtype == MLA_FP8_E4M3FN, stream),
+                    "kv write kernel");
+}
+
 int mla_up_project(void* k_nope_out, void* v_t_out, int32_t k_dtype, const void* latent,
                    const void* w_k, const void* w_uv, const int32_t* buffer_length_c,
                    int32_t num_heads, int32_t max_rows, hipStream_t stream) {

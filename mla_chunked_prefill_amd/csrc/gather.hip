@@ -121,6 +121,92 @@ gather_norm_rope_kernel(GatherArgs a) {
   }
 }
 
+// KV write path ("mla_prefill_decode_graph_bf16" page: Parameters
+// "kv_input_fn", the new tokens' raw latent rows [tot_seq_len, 576]; Args
+// "kv_norm_gamma", "epsilon", "freqs_cis", "input_row_offsets" and the paged
+// KV cache). Token t of sequence b (input_row_offsets[b] <= t <
+// input_row_offsets[b+1]) sits at position p = cache_lengths[b] + t -
+// input_row_offsets[b]; its row is normalised and rotated exactly as the
+// gather above does for a cache row, then stored in the pool slot of p. One
+// wave per token, the same 16-byte loads and stores; tokens whose page or
+// position is out of range are skipped.
+template <bool kFp8Cache>
+__global__ void __launch_bounds__(64 * kGatherRowsPerBlock) kv_write_kernel(KvWriteArgs a) {
+  const int t = blockIdx.x * kGatherRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= a.total || (uint32_t)t >= a.offs[a.B]) return;
+  const int lane = lane_id();
+  const int b = find_seq(a.offs, a.B, (uint32_t)t);
+  const uint32_t p = a.clen[b] + ((uint32_t)t - a.offs[b]);
+  const uint32_t lp = p / (uint32_t)a.ps;
+  const int page = lp < (uint32_t)a.maxp ? a.page_table[(size_t)b * a.maxp + lp] : -1;
+  if (page < 0 || page >= a.num_pages || p >= (uint32_t)a.max_seq_len) return;  // wave-uniform
+  const size_t slot = (size_t)page * a.ps + (p % (uint32_t)a.ps);
+
+  const uint16_t* in = a.input + (size_t)t * kCache;
+  const u32x4 v = *(const u32x4*)(in + lane * 8);
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(v[i]);
+    x[2 * i + 1] = bf16_hi(v[i]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss * (1.0f / kLora) + a.eps);
+  const u32x4 g = *(const u32x4*)(a.gamma + lane * 8);
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = x[2 * i] * inv * bf16_lo(g[i]);
+    o[2 * i + 1] = x[2 * i + 1] * inv * bf16_hi(g[i]);
+  }
+  float r[8];
+  if (lane < 8) {
+    const u32x4 y = *(const u32x4*)(in + kLora + lane * 8);
+    const u32x4 f = *(const u32x4*)(a.freqs + (size_t)p * kRope + lane * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y0 = bf16_lo(y[i]), y1 = bf16_hi(y[i]);
+      const float c = bf16_lo(f[i]), s = bf16_hi(f[i]);
+      r[2 * i] = y0 * c - y1 * s;
+      r[2 * i + 1] = y0 * s + y1 * c;
+    }
+  }
+  auto e4m3x8 = [](const float (&z)[8]) {
+    u32x2 w;
+    w[0] = f32_to_e4m3_sat(z[0]) | (f32_to_e4m3_sat(z[1]) << 8) | (f32_to_e4m3_sat(z[2]) << 16) |
+           (f32_to_e4m3_sat(z[3]) << 24);
+    w[1] = f32_to_e4m3_sat(z[4]) | (f32_to_e4m3_sat(z[5]) << 8) | (f32_to_e4m3_sat(z[6]) << 16) |
+           (f32_to_e4m3_sat(z[7]) << 24);
+    return w;
+  };
+  auto bf16x8_of = [](const float (&z)[8]) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(z[2 * i], z[2 * i + 1]);
+    return w;
+  };
+  if (kFp8Cache) {
+    uint8_t* rowp = (uint8_t*)a.cache + slot * kCache;
+    *(u32x2*)(rowp + lane * 8) = e4m3x8(o);
+    if (lane < 8) *(u32x2*)(rowp + kLora + lane * 8) = e4m3x8(r);
+  } else {
+    uint16_t* rowp = (uint16_t*)a.cache + slot * kCache;
+    *(u32x4*)(rowp + lane * 8) = bf16x8_of(o);
+    if (lane < 8) *(u32x4*)(rowp + kLora + lane * 8) = bf16x8_of(r);
+  }
+}
+
+hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8_cache, hipStream_t stream) {
+  const dim3 grid((a.total + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
+  const dim3 block(64 * kGatherRowsPerBlock);
+  if (fp8_cache) hipLaunchKernelGGL(kv_write_kernel<true>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(kv_write_kernel<false>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const GatherArgs& a, bool fp8_cache, bool fp8_rope,
                          hipStream_t stream) {
   const dim3 grid((a.max_rows + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);

@@ -17,6 +17,17 @@ struct GatherArgs {
   int B, ps, maxp, num_pages, max_rows, max_seq_len;
   float eps;
 };
+struct KvWriteArgs {
+  void* cache;               // [num_pages][ps][576] bf16 or e4m3fn, written
+  const int32_t* page_table; // [B][maxp]
+  const uint16_t* input;     // [total][576] bf16: the new tokens' raw rows
+  const uint32_t* offs;      // [B+1] input_row_offsets
+  const uint32_t* clen;      // [B] cache_lengths
+  const uint16_t* gamma;
+  const uint16_t* freqs;
+  int B, total, ps, maxp, num_pages, max_seq_len;
+  float eps;
+};
 struct GemmArgs {
   void* k_out;
   uint16_t* vt_out;
@@ -76,6 +87,7 @@ struct CombineArgs {
 hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,
                        const uint32_t*, int, int, uint32_t, hipStream_t);
 hipError_t launch_gather(const GatherArgs&, bool, bool, hipStream_t);
+hipError_t launch_kv_write(const KvWriteArgs&, bool, hipStream_t);
 hipError_t launch_up_project(const GemmArgs&, bool, hipStream_t);
 int attn_num_slots(int B, int total_q);
 hipError_t launch_attn_schedule(int2*, const uint32_t*, int, int, hipStream_t);

@@ -55,6 +55,16 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert b"aligned" in lib.mla_last_error()
     assert lib.mla_decode(fake, fake, fake, odd, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
                           0.1, fake, 1 << 40, None) == -1
+    # KV write: null input, unsupported cache dtype, misaligned cache
+    assert lib.mla_kv_write(fake, 0, fake, None, fake, fake, fake, fake, 2, 10, 16, 4, 8, 64,
+                            1e-6, None) == -1
+    assert lib.mla_kv_write(fake, 7, fake, fake, fake, fake, fake, fake, 2, 10, 16, 4, 8, 64,
+                            1e-6, None) == -2
+    assert lib.mla_kv_write(odd, 0, fake, fake, fake, fake, fake, fake, 2, 10, 16, 4, 8, 64,
+                            1e-6, None) == -1
+    # no new tokens: nothing to do, nothing enqueued
+    assert lib.mla_kv_write(fake, 0, fake, fake, fake, fake, fake, fake, 2, 0, 16, 4, 8, 64,
+                            1e-6, None) == 0
     # max_rows not a multiple of 64
     assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
     # workspace too small

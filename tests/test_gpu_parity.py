@@ -7,6 +7,7 @@ up-projection) are checked per element against a bound derived from their
 rounding: one bf16 rounding of the result (relative 2^-8) plus fp32
 accumulation error.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -17,6 +18,7 @@ from oracle import oracle
 from workloads import (Dims, decode_recipe, make_decode, make_prefill, prefill_recipe,
                        prefill_recipe_lengths, f32_to_bf16_bits, f32_to_e4m3fn_codes)
 from workloads.device import bf16_bits, decode_tensors, fp8_bits, prefill_tensors
+from workloads.gen import rope_table_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -411,3 +413,96 @@ def test_decode_b64_fp8_sampled(B):
     ref = oracle.decode(wl, batch_indices=idx)
     assert np.isfinite(got).all()
     _assert_close(got[idx], ref, FP8_MAX)
+
+
+# ---------------------------------------------------------------------------
+# KV write path: new tokens normalised, rotated and stored in their slots
+# ---------------------------------------------------------------------------
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _dev_pool(pool, fp8):
+    if fp8:
+        return torch.from_numpy(np.ascontiguousarray(pool)).view(torch.float8_e4m3fn).cuda()
+    return _dev_bf16(pool)
+
+
+def _kv_raw(rng, n):
+    x = f32_to_bf16_bits((1.5 * rng.standard_normal((n, 576))).astype(np.float32))
+    gamma = f32_to_bf16_bits((1.0 + 0.3 * rng.standard_normal(512)).astype(np.float32))
+    return x, gamma
+
+
+def _stored_bound(r, fp8):
+    # one rounding of the fp32 result to the cache dtype (unit roundoff 2^-8
+    # for bf16, 2^-4 for e4m3 normals, half the 2^-9 subnormal step) plus the
+    # fp32 arithmetic of the norm and the rotation
+    if fp8:
+        return 2.0 ** -4 * np.abs(r) + 2.0 ** -10 + 1e-5
+    return (2.0 ** -8 + 2e-6) * np.abs(r) + 1e-5
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_kv_write_small(B, fp8):
+    rng = np.random.default_rng(61)
+    ps = 16
+    cached, new = [5, 0, 40, 7], [17, 1, 33, 0]
+    L = np.asarray(cached) + np.asarray(new)
+    maxp = int(((L + ps - 1) // ps).max()) + 1
+    num_pages = len(cached) * maxp + 3
+    pt = rng.permutation(num_pages)[:len(cached) * maxp].reshape(len(cached), maxp).astype(np.int32)
+    pt[2, 3] = -1                              # a missing page: its tokens are skipped
+    vals = rng.standard_normal((num_pages, ps, 576)).astype(np.float32)
+    pool = f32_to_e4m3fn_codes(vals) if fp8 else f32_to_bf16_bits(vals)
+    off = np.concatenate([[0], np.cumsum(new)]).astype(np.uint32)
+    x, gamma = _kv_raw(rng, int(off[-1]))
+    max_seq_len = int(L.max()) - 3             # the last three positions have no rotation row
+    freqs = rope_table_bits(max_seq_len, 64)
+    cache = _dev_pool(pool, fp8)
+    B.mla_kv_write(cache, torch.from_numpy(pt).cuda(), _dev_bf16(x), _u32(off), _u32(cached),
+                   _dev_bf16(gamma), _dev_bf16(freqs), 1e-6)
+    torch.cuda.synchronize()
+    got_bits = fp8_bits(cache) if fp8 else bf16_bits(cache)
+    dec = oracle.e4m3fn_to_f64 if fp8 else oracle.bf16_to_f64
+    ref = oracle.kv_write(dec(pool), pt, oracle.bf16_to_f64(x), off, cached,
+                          oracle.bf16_to_f64(gamma), oracle.bf16_to_f64(freqs), 1e-6, ps)
+    written = np.zeros(pool.shape[:2], dtype=bool)
+    for b in range(len(cached)):
+        for i in range(new[b]):
+            p = cached[b] + i
+            if pt[b, p // ps] >= 0 and p < max_seq_len:
+                written[pt[b, p // ps], p % ps] = True
+    assert 0 < written.sum() < sum(new)       # the hole and the short table removed some
+    assert np.array_equal(got_bits[~written], pool[~written])     # nothing else touched
+    g, r = dec(got_bits)[written], ref[written]
+    assert (np.abs(g - r) <= _stored_bound(r, fp8)).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_kv_write_then_decode(B, fp8):
+    # decode reads rows as stored: write each sequence's new token from its raw
+    # row, then decode; the oracle decodes the pool the write defines
+    wl = make_decode("kvw", 71, [300, 1, 1000, 77], 16, 16, fp8=fp8)
+    ctx = wl.context_lens.astype(np.int64)
+    rng = np.random.default_rng(72)
+    x, gamma = _kv_raw(rng, len(ctx))
+    freqs = rope_table_bits(int(ctx.max()), 64)
+    off = np.arange(len(ctx) + 1, dtype=np.uint32)
+    t = decode_tensors(wl)
+    B.mla_kv_write(t["kv_cache"], t["page_table"], _dev_bf16(x), _u32(off), _u32(ctx - 1),
+                   _dev_bf16(gamma), _dev_bf16(freqs), 1e-6)
+    out = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
+                   t["w_uv"], int(ctx.max()), wl.scale)
+    torch.cuda.synchronize()
+    dec = oracle.e4m3fn_to_f64 if fp8 else oracle.bf16_to_f64
+    vals = oracle.kv_write(dec(wl.pool), wl.page_table, oracle.bf16_to_f64(x), off, ctx - 1,
+                           oracle.bf16_to_f64(gamma), oracle.bf16_to_f64(freqs), 1e-6,
+                           wl.page_size).astype(np.float32)
+    stored = f32_to_e4m3fn_codes(vals) if fp8 else f32_to_bf16_bits(vals)
+    ref = oracle.decode(dataclasses.replace(wl, pool=stored))
+    if fp8:
+        _assert_close(_f64(out), ref, FP8_MAX)
+    else:
+        _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
