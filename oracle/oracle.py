@@ -430,6 +430,28 @@ def decode(wl, dec: DecodedDecode | None = None, batch_indices=None) -> np.ndarr
     return out
 
 
+def decode_sparse(q: np.ndarray, pool: np.ndarray, d_indices: np.ndarray, topk_lengths,
+                  w_uk: np.ndarray, w_uv: np.ndarray, scale: float, nope: int = 128,
+                  lora: int = 512) -> np.ndarray:
+    """Sparse absorbed decode (mla_prefill_decode_graph_bf16 page: Parameters
+    "sparse_mla", "sparse_indices_stride"; Args "d_indices" (physical KV row
+    indices per sequence), "indices_stride", "topk_lengths"): token b attends
+    over the pool rows d_indices[b, 0:topk_lengths[b]] as stored, a physical
+    row being page * page_size + slot of the pool flattened to rows. A
+    sequence that lists no row outputs zeros. Values, not storage bits.
+    Returns [B, H, v]."""
+    flat = np.asarray(pool, dtype=np.float64).reshape(-1, pool.shape[-1])
+    q = np.asarray(q, dtype=np.float64)
+    out = np.zeros((q.shape[0], w_uv.shape[0], w_uv.shape[1]))
+    for b in range(q.shape[0]):
+        k = int(topk_lengths[b])
+        if k <= 0:
+            continue
+        Z = flat[np.asarray(d_indices[b, :k], dtype=np.int64)]
+        out[b] = decode_one(q[b], Z, w_uk, w_uv, scale, nope, lora)
+    return out
+
+
 def decode_split(wl, num_splits: int, dec: DecodedDecode | None = None) -> np.ndarray:
     """Decode with the context cut into num_splits parts whose partial softmax
     states are merged by log-sum-exp; reaches decode() up to rounding."""

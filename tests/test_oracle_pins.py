@@ -438,3 +438,49 @@ def test_kv_write_rotates_by_the_position_angle():
     assert np.allclose(out[0, 5, 512::2], np.cos(ang[5]), atol=1e-15)
     assert np.allclose(out[0, 5, 513::2], np.sin(ang[5]), atol=1e-15)
     assert np.array_equal(out[0, :5], pool[0, :5]) and np.array_equal(out[0, 6:], pool[0, 6:])
+
+
+# ---------------------------------------------------------------------------
+# Sparse decode: attention over an explicit list of pool rows
+# ---------------------------------------------------------------------------
+
+def _sparse_inputs(seed=21, ctx=(5, 40, 1), H=4):
+    wl = make_decode("sp", seed, list(ctx), H, 8, dims=Dims(nope=16, rope=8, v=16, lora=32))
+    dec = oracle.DecodedDecode(wl)
+    ps = wl.page_size
+    idx = np.zeros((len(ctx), max(ctx) + 3), dtype=np.int32)
+    for b, n in enumerate(ctx):   # the physical row of every position, in order
+        for p in range(n):
+            idx[b, p] = wl.page_table[b, p // ps] * ps + p % ps
+    return wl, dec, idx
+
+
+def test_sparse_decode_over_the_context_in_order_is_decode():
+    wl, dec, idx = _sparse_inputs()
+    got = oracle.decode_sparse(dec.q, dec.pool, idx, wl.context_lens, dec.w_uk, dec.w_uv,
+                               wl.scale, dec.nope, dec.lora)
+    assert np.allclose(got, oracle.decode(wl), rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_decode_is_a_set_function_and_a_single_row_returns_its_projection():
+    wl, dec, idx = _sparse_inputs(seed=22, ctx=(30, 1, 12))
+    rng = np.random.default_rng(3)
+    shuffled = idx.copy()
+    for b, n in enumerate(wl.context_lens):
+        shuffled[b, :n] = rng.permutation(idx[b, :n])
+    a = oracle.decode_sparse(dec.q, dec.pool, idx, wl.context_lens, dec.w_uk, dec.w_uv,
+                             wl.scale, dec.nope, dec.lora)
+    c = oracle.decode_sparse(dec.q, dec.pool, shuffled, wl.context_lens, dec.w_uk, dec.w_uv,
+                             wl.scale, dec.nope, dec.lora)
+    assert np.allclose(a, c, rtol=1e-12, atol=1e-14)
+    # sequence 1 lists one row: softmax weight 1, output w_uv[h] @ that row's latent
+    z = dec.pool.reshape(-1, dec.pool.shape[-1])[idx[1, 0], :dec.lora]
+    assert np.allclose(a[1], np.einsum("hdl,l->hd", dec.w_uv, z), rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_decode_of_an_empty_list_is_zero():
+    wl, dec, idx = _sparse_inputs()
+    lens = np.array([5, 0, 1])
+    got = oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
+                               dec.nope, dec.lora)
+    assert np.array_equal(got[1], np.zeros_like(got[1])) and np.abs(got[0]).sum() > 0
