@@ -11,7 +11,8 @@ per-call durations; the attention call is the dominant kernel.
 
 A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
 batch (contexts U{4096..32768}), with a bf16 and then an e4m3 cache, and
-reports achieved HBM bandwidth. A third times mla_kv_write storing the
+reports achieved HBM bandwidth, then mla_decode_sparse with every sequence
+listing 2048 rows of its context. A last phase times mla_kv_write storing the
 prompt's 4096 new tokens into the paged cache (normalised, rotated).
 
 Before the W warm-up steps, about S seconds (default 1) of the same work run
@@ -197,6 +198,54 @@ def bench_decode(args, binding, torch, recipe="decode_b64"):
     return dict(ms=ms, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows)
 
 
+def bench_decode_sparse(args, binding, torch, topk=2048):
+    """mla_decode_sparse on decode_b64's pool, queries and weights: every
+    sequence lists `topk` distinct rows of its own context (uniform positions,
+    sorted, mapped through its page table)."""
+    import numpy as np
+    from workloads import decode_recipe
+    from workloads.device import decode_tensors
+
+    wl = decode_recipe("decode_b64")
+    t = decode_tensors(wl)
+    B, H = wl.batch, wl.num_heads
+    rng = np.random.default_rng(10)
+    ps = wl.page_size
+    idx = np.zeros((B, topk), dtype=np.int32)
+    for b in range(B):
+        pos = np.sort(rng.choice(int(wl.context_lens[b]), size=topk, replace=False))
+        idx[b] = wl.page_table[b, pos // ps] * ps + pos % ps
+    d_idx = torch.from_numpy(idx).cuda()
+    lens = torch.full((B,), topk, dtype=torch.int32, device="cuda")
+    rows = t["kv_cache"].reshape(-1, 576)
+    out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(binding.mla_decode_sparse_workspace_size(B, H, topk, 0, binding.MLA_BF16),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        binding.mla_decode_sparse(out, t["q"], lens, rows, d_idx, t["w_uk"], t["w_uv"], topk,
+                                  wl.scale, ws)
+
+    warm_clock(call, args.warm_seconds / 4, torch)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    nrows = B * topk
+    bytes_alg = nrows * 576 * 2 + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2 + nrows * 4
+    flop = 2 * (576 + 512) * H * nrows
+    return dict(ms=ms, bytes=bytes_alg, flop=flop)
+
+
 def bench_kv_write(args, binding, torch):
     """mla_kv_write on the prompt of dsv3_prefill_4k: 4096 new tokens' raw
     576-wide rows normalised, rotated and stored in a bf16 pool of 128-row
@@ -363,6 +412,17 @@ def main():
             "tflops": round(d8["flop"] / (d8["ms"] * 1e-3) / 1e12, 2),
             "split_kernel_traffic": load_traffic("decode.hip",
                                                  "decode_split_decode_b64_fp8_counters.json"),
+        }
+        ds = bench_decode_sparse(args, binding, torch)
+        gbps = ds["bytes"] / (ds["ms"] * 1e-3) / 1e9
+        line["decode_sparse"] = {
+            "workload": "mla_decode_sparse: decode_b64's 64 sequences, each attending over "
+                        "2048 distinct rows of its own context listed by physical index",
+            "ms": round(ds["ms"], 4),
+            "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": ds["bytes"],
+            "tflops": round(ds["flop"] / (ds["ms"] * 1e-3) / 1e12, 2),
         }
     kw = bench_kv_write(args, binding, torch)
     gbps = kw["bytes"] / (kw["ms"] * 1e-3) / 1e9

@@ -297,15 +297,16 @@ int mla_prefill(void* output, const void* q, int32_t dtype,
  *
  *   output     bf16 [batch_size, num_heads, 128]
  *   q          bf16 [batch_size, num_heads, 192]
- *   context_lengths uint32 [batch_size]  (>= 1, includes the new token)
+ *   context_lengths uint32 [batch_size]  (includes the new token; 0 gives zeros)
  *   kv_cache   bf16 or e4m3 (cache_dtype) [num_pages, page_size, 576]
  *   page_table int32 [batch_size, max_pages_per_seq]
  *   w_uk bf16 [num_heads, 512, 128]; w_uv bf16 [num_heads, 128, 512]
- *   max_context_len: host upper bound on every context length
+ *   max_context_len: host upper bound on every context length (a longer
+ *   device value counts as max_context_len; its result is unspecified)
  *   Limits: num_heads <= 128; batch_size * max_context_len < 2^31;
  *   num_pages * page_size < 2^31.
- * With an e4m3 cache both products run on fp8 MFMA (q_lat and the softmax
- * weights are rounded to e4m3).
+ * With an e4m3 cache the rows are widened exactly to bf16 (every e4m3fn value
+ * is a bf16 number) and both products run on bf16 MFMA with a bf16 q_lat.
  */
 size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads,
                                  int32_t max_context_len, int32_t page_size,
@@ -320,6 +321,40 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
 /* Text for a status code, and the message of the calling thread's last failure. */
 const char* mla_status_string(int status);
 const char* mla_last_error(void);
+
+/*
+ * mla_decode_sparse_workspace_size / mla_decode_sparse -- absorbed decode of
+ * one new token per sequence over an explicit list of cache rows
+ * ("mla_prefill_decode_graph_bf16" page: Parameters "sparse_mla",
+ * "sparse_indices_stride"; Args "d_indices", "indices_stride",
+ * "topk_lengths").
+ *
+ * Sequence b attends over the pool rows d_indices[b * indices_stride + j],
+ * j < topk_lengths[b], exactly as mla_decode attends over a context (rows used
+ * as stored; a row is page * page_size + slot of the pool viewed as
+ * [num_rows, 576]). Rows may repeat (a repeated row counts twice). A sequence
+ * that lists no row outputs zeros.
+ *
+ *   output       bf16 [batch_size, num_heads, 128]   (device, written)
+ *   q            bf16 [batch_size, num_heads, 192]
+ *   topk_lengths int32 [batch_size], each in [0, max_topk]
+ *   kv_cache     bf16 or e4m3 [num_rows, 576] (cache_dtype)
+ *   d_indices    int32 [batch_size, indices_stride], each in [0, num_rows)
+ *   w_uk, w_uv, num_heads, num_partitions, scale: as mla_decode.
+ * max_topk <= indices_stride. The workspace holds at least
+ * mla_decode_sparse_workspace_size(batch_size, num_heads, max_topk,
+ * num_partitions, cache_dtype) bytes. Lengths above max_topk count as
+ * max_topk; indices outside [0, num_rows) read row 0; the results of such
+ * sequences are unspecified.
+ */
+size_t mla_decode_sparse_workspace_size(int32_t batch_size, int32_t num_heads, int32_t max_topk,
+                                        int32_t num_partitions, int32_t cache_dtype);
+int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
+                      const void* kv_cache, int32_t cache_dtype, const int32_t* d_indices,
+                      int32_t indices_stride, const void* w_uk, const void* w_uv,
+                      int32_t batch_size, int32_t num_heads, int32_t num_rows, int32_t max_topk,
+                      int32_t num_partitions, float scale, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

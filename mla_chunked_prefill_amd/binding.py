@@ -44,6 +44,9 @@ _SIGNATURES = {
     "mla_decode_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "mla_decode": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                         _P, _S, _P]),
+    "mla_decode_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "mla_decode_sparse": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F,
+                               _P, _S, _P]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -278,6 +281,33 @@ def mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
     _check("mla_decode", st)
 
 
+def mla_decode_sparse_workspace_size(batch_size: int, num_heads: int, max_topk: int,
+                                     num_partitions: int, cache_dtype: int) -> int:
+    return int(load().mla_decode_sparse_workspace_size(batch_size, num_heads, max_topk,
+                                                       num_partitions, cache_dtype))
+
+
+def mla_decode_sparse(output, q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: int,
+                      scale: float, workspace, num_partitions: int = 0, stream=None):
+    B, H = q.shape[0], q.shape[1]
+    _expect(output, torch.bfloat16, (B, H, VD), "output")
+    _expect(q, torch.bfloat16, (B, H, QD), "q")
+    _expect(topk_lengths, torch.int32, (B,), "topk_lengths")
+    _expect(d_indices, torch.int32, None, "d_indices")
+    if d_indices.dim() != 2 or d_indices.shape[0] != B:
+        raise ValueError("d_indices shape")
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != CACHE:
+        raise ValueError("kv_cache shape: [num_rows, 576]")
+    _expect(w_uk, torch.bfloat16, (H, LORA, NOPE), "w_uk")
+    _expect(w_uv, torch.bfloat16, (H, VD, LORA), "w_uv")
+    st = load().mla_decode_sparse(
+        _ptr(output), _ptr(q), _ptr(topk_lengths), _ptr(kv_cache), _dtype_code(kv_cache),
+        _ptr(d_indices), d_indices.shape[1], _ptr(w_uk), _ptr(w_uv), B, H, kv_cache.shape[0],
+        int(max_topk), int(num_partitions), float(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mla_decode_sparse", st)
+
+
 # ---------------------------------------------------------------------------
 # convenience: plan + workspace + call
 # ---------------------------------------------------------------------------
@@ -335,4 +365,22 @@ def decode(q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
     mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len,
                scale, workspace, num_partitions=num_partitions, stream=stream)
+    return output
+
+
+def decode_sparse(q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: int,
+                  scale: float, num_partitions: int = 0, workspace=None, output=None,
+                  stream=None):
+    """Sparse absorbed decode over the listed pool rows; returns [B, H, 128] bf16.
+    kv_cache may be given paged ([num_pages, page_size, 576]); it is viewed as rows."""
+    B, H = q.shape[0], q.shape[1]
+    rows = kv_cache.reshape(-1, CACHE)
+    if output is None:
+        output = torch.empty((B, H, VD), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        nbytes = mla_decode_sparse_workspace_size(B, H, max_topk, num_partitions,
+                                                  _dtype_code(kv_cache))
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    mla_decode_sparse(output, q, topk_lengths, rows, d_indices, w_uk, w_uv, max_topk, scale,
+                      workspace, num_partitions=num_partitions, stream=stream)
     return output

@@ -462,8 +462,9 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                                                 stream),
                       "absorb kernel");
   if (st != MLA_OK) return st;
-  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size, ws.wstart,
-                                            ws.wspan, ws.wfirst, ws.G, stream),
+  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size,
+                                            max_context_len, ws.wstart, ws.wspan, ws.wfirst,
+                                            ws.G, stream),
                   "prefix kernel");
   if (st != MLA_OK) return st;
   mla::DecodeArgs a;
@@ -508,6 +509,30 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                                                (const uint16_t*)w_uv, batch_size, num_heads,
                                                stream),
                     "projection kernel");
+}
+
+size_t mla_decode_sparse_workspace_size(int32_t batch_size, int32_t num_heads, int32_t max_topk,
+                                        int32_t num_partitions, int32_t cache_dtype) {
+  return mla_decode_workspace_size(batch_size, num_heads, max_topk, 1, num_partitions,
+                                   cache_dtype);
+}
+
+// The listed rows are a paged context with one row per page: the index list
+// is the page table, the pool's rows its pages.
+int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
+                      const void* kv_cache, int32_t cache_dtype, const int32_t* d_indices,
+                      int32_t indices_stride, const void* w_uk, const void* w_uv,
+                      int32_t batch_size, int32_t num_heads, int32_t num_rows, int32_t max_topk,
+                      int32_t num_partitions, float scale, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!topk_lengths || !d_indices) return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: null pointer");
+  if (indices_stride < 1 || num_rows < 1 || max_topk < 1 || max_topk > indices_stride)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: indices_stride=%d num_rows=%d max_topk=%d",
+                indices_stride, num_rows, max_topk);
+  return mla_decode(output, q, (const uint32_t*)topk_lengths, kv_cache, cache_dtype, d_indices,
+                    w_uk, w_uv, batch_size, num_heads, 1, indices_stride, num_rows,
+                    max_topk, num_partitions, scale, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

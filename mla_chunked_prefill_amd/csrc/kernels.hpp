@@ -95,8 +95,8 @@ hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
 hipError_t launch_decode_absorb(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                 hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
-hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, uint32_t*, int2*, int32_t*,
-                                int, hipStream_t);
+hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, int, uint32_t*, int2*,
+                                int32_t*, int, hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);

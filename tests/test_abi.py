@@ -65,6 +65,13 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     # no new tokens: nothing to do, nothing enqueued
     assert lib.mla_kv_write(fake, 0, fake, fake, fake, fake, fake, fake, 2, 0, 16, 4, 8, 64,
                             1e-6, None) == 0
+    # sparse decode: max_topk beyond the index stride; no index list
+    need = lib.mla_decode_sparse_workspace_size(4, 8, 100, 0, 0)
+    assert need > 0
+    assert lib.mla_decode_sparse(fake, fake, fake, fake, 0, fake, 64, fake, fake, 4, 8, 1000, 100,
+                                 0, 0.1, fake, need, None) == -1
+    assert lib.mla_decode_sparse(fake, fake, fake, fake, 0, None, 128, fake, fake, 4, 8, 1000, 100,
+                                 0, 0.1, fake, need, None) == -1
     # max_rows not a multiple of 64
     assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
     # workspace too small

@@ -506,3 +506,56 @@ def test_kv_write_then_decode(B, fp8):
         _assert_close(_f64(out), ref, FP8_MAX)
     else:
         _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
+
+
+# ---------------------------------------------------------------------------
+# sparse decode: attention over explicit lists of pool rows
+# ---------------------------------------------------------------------------
+
+def _sparse_case(wl, lens, seed):
+    rng = np.random.default_rng(seed)
+    rows = wl.pool.shape[0] * wl.pool.shape[1]
+    stride = max(lens) + 3
+    idx = rng.integers(0, rows, size=(len(lens), stride)).astype(np.int32)
+    idx[0, :] = idx[0, 0]                      # the same row listed over and over
+    return idx
+
+
+def _run_sparse(B, wl, idx, lens):
+    t = decode_tensors(wl)
+    out = B.decode_sparse(t["q"], torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                          t["kv_cache"], torch.from_numpy(idx).cuda(), t["w_uk"], t["w_uv"],
+                          idx.shape[1], wl.scale)
+    torch.cuda.synchronize()
+    return _f64(out)
+
+
+def _sparse_ref(wl, idx, lens):
+    dec = oracle.DecodedDecode(wl)
+    return oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
+                                dec.nope, dec.lora)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_sparse_small(B, fp8):
+    wl = make_decode("sp", 81, [2000, 900, 3000, 40, 1500], 16, 16, fp8=fp8)
+    lens = [5, 37, 300, 0, 700]
+    idx = _sparse_case(wl, lens, 82)
+    got = _run_sparse(B, wl, idx, lens)
+    ref = _sparse_ref(wl, idx, lens)
+    assert np.array_equal(got[3], np.zeros_like(got[3]))      # an empty list gives zeros
+    if fp8:
+        _assert_close(got, ref, FP8_MAX)
+    else:
+        _assert_close(got, ref, BF16_MAX, BF16_MEAN)
+
+
+def test_decode_sparse_over_the_context_in_order_equals_decode(B):
+    wl = make_decode("spd", 83, [1, 37, 300, 64, 1000], 128, 16)
+    ps = wl.page_size
+    ctx = [int(c) for c in wl.context_lens]
+    idx = np.zeros((len(ctx), max(ctx)), dtype=np.int32)
+    for b, n in enumerate(ctx):
+        p = np.arange(n)
+        idx[b, :n] = wl.page_table[b, p // ps] * ps + p % ps
+    _assert_close(_run_sparse(B, wl, idx, ctx), oracle.decode(wl), BF16_MAX, BF16_MEAN)
