@@ -257,21 +257,32 @@ class Decoded:
 # ---------------------------------------------------------------------------
 
 
-def _masked_softmax_rows(s: np.ndarray, visible: np.ndarray) -> np.ndarray:
+def _masked_softmax_rows(s: np.ndarray, visible: np.ndarray, sink=None) -> np.ndarray:
+    """Softmax of the visible scores of every row. A sink (mla_prefill_decode
+    _graph_bf16 page: Args "attn_sink_ptr", per-batch attention sink weights)
+    is one more logit in the denominator whose value vector is zero: weights
+    e^s_j / (sum_k e^s_k + e^sink). A row with no visible key and a sink gets
+    all-zero weights."""
     s = np.where(visible, s, -np.inf)
     m = np.max(s, axis=-1, keepdims=True)
+    if sink is not None and np.isfinite(sink):
+        m = np.maximum(m, sink)
     e = np.where(visible, np.exp(s - m), 0.0)
-    return e / np.sum(e, axis=-1, keepdims=True)
+    den = np.sum(e, axis=-1, keepdims=True)
+    if sink is not None and np.isfinite(sink):
+        den = den + np.exp(sink - m)
+    return e / den
 
 
 def attend_sequence(qb: np.ndarray, k_nope: np.ndarray, krope: np.ndarray,
                     v: np.ndarray, qpos: np.ndarray, kpos: np.ndarray,
-                    scale: float, nope: int) -> np.ndarray:
+                    scale: float, nope: int, sink=None) -> np.ndarray:
     """Attention of one sequence's queries over its keys, all heads.
 
     qb [n, H, nope+rope]; k_nope [L, H, nope]; krope [L, rope] (one head shared
     by all query heads); v [L, H, v]. Query at absolute position qpos[i] sees the
-    key at kpos[j] iff kpos[j] <= qpos[i]. Returns [n, H, v].
+    key at kpos[j] iff kpos[j] <= qpos[i]. sink: the sequence's sink logit, or
+    None. Returns [n, H, v].
     """
     n, H = qb.shape[0], qb.shape[1]
     out = np.empty((n, H, v.shape[-1]))
@@ -279,13 +290,14 @@ def attend_sequence(qb: np.ndarray, k_nope: np.ndarray, krope: np.ndarray,
     rope_scores = np.einsum("nhe,le->hnl", qb[:, :, nope:], krope)
     for h in range(H):
         s = qb[:, h, :nope] @ k_nope[:, h, :].T + rope_scores[h]
-        a = _masked_softmax_rows(scale * s, visible)
+        a = _masked_softmax_rows(scale * s, visible, sink)
         out[:, h, :] = a @ v[:, h, :]
     return out
 
 
-def prefill(wl, dec: Decoded | None = None) -> np.ndarray:
-    """Full MLA prefill output [T_q, H, v] in float64 (no chunking)."""
+def prefill(wl, dec: Decoded | None = None, sinks=None) -> np.ndarray:
+    """Full MLA prefill output [T_q, H, v] in float64 (no chunking); sinks:
+    one sink logit per sequence, or None."""
     dec = dec or Decoded(wl)
     out = np.zeros((wl.total_q, dec.H, dec.v))
     for b in range(dec.B):
@@ -298,7 +310,7 @@ def prefill(wl, dec: Decoded | None = None) -> np.ndarray:
         qpos = dec.clen[b] + np.arange(n)
         out[dec.offs[b]:dec.offs[b + 1]] = attend_sequence(
             dec.q[dec.offs[b]:dec.offs[b + 1]], k_nope, krope, v, qpos,
-            np.arange(L), wl.scale, dec.nope)
+            np.arange(L), wl.scale, dec.nope, None if sinks is None else float(sinks[b]))
     return out
 
 
@@ -402,37 +414,37 @@ class DecodedDecode:
 
 
 def decode_one(qrow: np.ndarray, Z: np.ndarray, w_uk: np.ndarray, w_uv: np.ndarray,
-               scale: float, nope: int, lora: int) -> np.ndarray:
+               scale: float, nope: int, lora: int, sink=None) -> np.ndarray:
     """Absorbed decode of one token, all heads.
 
     qrow [H, nope+rope]; Z [ctx, lora+rope] cache rows as stored (one KV head);
     q_lat[h] = w_uk[h] @ q_nope[h]; s = scale * (q_lat . Z[:, :lora] +
     q_rope . Z[:, lora:]); o_lat = softmax(s) @ Z[:, :lora]; out[h] = w_uv[h] @ o_lat.
-    Returns [H, v].
+    sink: a sink logit in the softmax denominator, or None. Returns [H, v].
     """
     qlat = np.einsum("hld,hd->hl", w_uk, qrow[:, :nope])
     s = scale * (qlat @ Z[:, :lora].T + qrow[:, nope:] @ Z[:, lora:].T)
-    m = np.max(s, axis=1, keepdims=True)
-    e = np.exp(s - m)
-    a = e / np.sum(e, axis=1, keepdims=True)
+    a = _masked_softmax_rows(s, np.ones(s.shape, dtype=bool), sink)
     olat = a @ Z[:, :lora]
     return np.einsum("hdl,hl->hd", w_uv, olat)
 
 
-def decode(wl, dec: DecodedDecode | None = None, batch_indices=None) -> np.ndarray:
-    """Absorbed decode output [B, H, v] (or only the listed sequences)."""
+def decode(wl, dec: DecodedDecode | None = None, batch_indices=None, sinks=None) -> np.ndarray:
+    """Absorbed decode output [B, H, v] (or only the listed sequences); sinks:
+    one sink logit per sequence, or None."""
     dec = dec or DecodedDecode(wl)
     idx = range(len(dec.ctx)) if batch_indices is None else list(batch_indices)
     out = np.zeros((len(idx), dec.H, dec.v))
     for i, b in enumerate(idx):
         Z = gather_rows(dec.pool, wl.page_table, b, np.arange(dec.ctx[b]), wl.page_size)
-        out[i] = decode_one(dec.q[b], Z, dec.w_uk, dec.w_uv, wl.scale, dec.nope, dec.lora)
+        out[i] = decode_one(dec.q[b], Z, dec.w_uk, dec.w_uv, wl.scale, dec.nope, dec.lora,
+                            None if sinks is None else float(sinks[b]))
     return out
 
 
 def decode_sparse(q: np.ndarray, pool: np.ndarray, d_indices: np.ndarray, topk_lengths,
                   w_uk: np.ndarray, w_uv: np.ndarray, scale: float, nope: int = 128,
-                  lora: int = 512) -> np.ndarray:
+                  lora: int = 512, sinks=None) -> np.ndarray:
     """Sparse absorbed decode (mla_prefill_decode_graph_bf16 page: Parameters
     "sparse_mla", "sparse_indices_stride"; Args "d_indices" (physical KV row
     indices per sequence), "indices_stride", "topk_lengths"): token b attends
@@ -448,7 +460,8 @@ def decode_sparse(q: np.ndarray, pool: np.ndarray, d_indices: np.ndarray, topk_l
         if k <= 0:
             continue
         Z = flat[np.asarray(d_indices[b, :k], dtype=np.int64)]
-        out[b] = decode_one(q[b], Z, w_uk, w_uv, scale, nope, lora)
+        out[b] = decode_one(q[b], Z, w_uk, w_uv, scale, nope, lora,
+                            None if sinks is None else float(sinks[b]))
     return out
 
 

@@ -5,6 +5,7 @@ a wrong sign, an off-by-one mask, a transposed operand, a wrong pairing) fails
 at least one of them. None of them re-types an oracle formula or re-calls the
 oracle's own library routine on the same expression.
 """
+import dataclasses
 import itertools
 import math
 
@@ -484,3 +485,47 @@ def test_sparse_decode_of_an_empty_list_is_zero():
     got = oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
                                dec.nope, dec.lora)
     assert np.array_equal(got[1], np.zeros_like(got[1])) and np.abs(got[0]).sum() > 0
+
+
+# ---------------------------------------------------------------------------
+# attention sinks: one more logit in the softmax denominator
+# ---------------------------------------------------------------------------
+
+def test_sink_with_zero_query_divides_the_prefix_sum_by_count_plus_exp_sink():
+    # q = 0 makes every score 0: each visible key weighs 1 / (n + e^sink)
+    wl = _tiny_prefill(4, [5, 3], [2, 0])
+    wl = _with_q(wl, np.zeros(wl.q.shape))
+    dec = oracle.Decoded(wl)
+    sinks = np.array([0.7, -1.3])
+    out = oracle.prefill(wl, dec, sinks=sinks)
+    for b in range(2):
+        latn, _ = dec.seq_keys(b)
+        _, v = oracle.up_project(latn, dec.w_k, dec.w_uv, dec.H)
+        for i in range(dec.offs[b + 1] - dec.offs[b]):
+            P = dec.clen[b] + i
+            expect = v[:P + 1].sum(axis=0) / (P + 1 + math.exp(sinks[b]))
+            assert np.allclose(out[dec.offs[b] + i], expect, rtol=1e-12)
+
+
+def test_sink_of_minus_infinity_is_no_sink_and_a_huge_sink_silences():
+    wl = _tiny_prefill(4, [5, 3], [2, 0])
+    dec = oracle.Decoded(wl)
+    base = oracle.prefill(wl, dec)
+    assert np.array_equal(oracle.prefill(wl, dec, sinks=np.array([-np.inf, -np.inf])), base)
+    quiet = oracle.prefill(wl, dec, sinks=np.array([200.0, 200.0]))
+    assert np.abs(quiet).max() < 1e-60
+    dwl = make_decode("sk", 31, [7, 1, 20], 4, 4, dims=Dims(nope=16, rope=8, v=16, lora=32))
+    ddec = oracle.DecodedDecode(dwl)
+    assert np.array_equal(oracle.decode(dwl, ddec, sinks=np.full(3, -np.inf)), oracle.decode(dwl, ddec))
+
+
+def test_decode_sink_with_zero_query_closed_form():
+    dwl = make_decode("sk0", 32, [7, 1, 20], 4, 4, dims=Dims(nope=16, rope=8, v=16, lora=32))
+    dwl = dataclasses.replace(dwl, q=np.zeros_like(dwl.q))
+    ddec = oracle.DecodedDecode(dwl)
+    sinks = np.array([1.5, -0.25, 3.0])
+    out = oracle.decode(dwl, ddec, sinks=sinks)
+    for b, n in enumerate(ddec.ctx):
+        Z = oracle.gather_rows(ddec.pool, dwl.page_table, b, np.arange(n), dwl.page_size)
+        olat = Z[:, :ddec.lora].sum(axis=0) / (n + math.exp(sinks[b]))
+        assert np.allclose(out[b], np.einsum("hdl,l->hd", ddec.w_uv, olat), rtol=1e-12)
