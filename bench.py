@@ -160,7 +160,7 @@ def bench_prefill(args, binding, torch):
         attn_flop=attn_flop, gemm_flop=gemm_flop, pairs=pairs, max_rows=max_rows)
 
 
-def bench_decode(args, binding, torch, recipe="decode_b64"):
+def bench_decode(args, binding, torch, recipe="decode_b64", sinks=False):
     from workloads import decode_recipe
     from workloads.device import decode_tensors
 
@@ -173,9 +173,11 @@ def bench_decode(args, binding, torch, recipe="decode_b64"):
     ws = torch.empty(binding.mla_decode_workspace_size(B, H, max_ctx, wl.page_size, 0, code),
                      dtype=torch.uint8, device="cuda")
 
+    sink = torch.linspace(-2.0, 2.0, B, device="cuda", dtype=torch.float32) if sinks else None
+
     def call():
         binding.mla_decode(out, t["q"], t["context_lengths"], t["kv_cache"], t["page_table"],
-                           t["w_uk"], t["w_uv"], max_ctx, wl.scale, ws)
+                           t["w_uk"], t["w_uv"], max_ctx, wl.scale, ws, attn_sink=sink)
 
     warm_clock(call, args.warm_seconds / 2, torch)
     for _ in range(args.warmup):
@@ -413,6 +415,8 @@ def main():
             "split_kernel_traffic": load_traffic("decode.hip",
                                                  "decode_split_decode_b64_fp8_counters.json"),
         }
+        dk = bench_decode(args, binding, torch, sinks=True)
+        line["decode"]["ms_with_sinks"] = round(dk["ms"], 4)
         ds = bench_decode_sparse(args, binding, torch)
         gbps = ds["bytes"] / (ds["ms"] * 1e-3) / 1e9
         line["decode_sparse"] = {

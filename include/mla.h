@@ -32,6 +32,12 @@
  *   MLA_ERR_INVALID_ARG.
  *   "bf16" is bfloat16, "e4m3" is OCP float8_e4m3fn (1-4-3, bias 7, no
  *   infinities), each passed as raw storage.
+ * - Attention sinks ("mla_prefill_decode_graph_bf16" page, Args
+ *   "attn_sink_ptr": optional per-batch attention sink weights): the
+ *   attention entry points take attn_sink, float32 [batch_size] or null. A
+ *   sequence's sink is one more logit, in the units of the scaled scores, in
+ *   the softmax denominator with a zero value vector: weights become
+ *   e^s_j / (sum_k e^s_k + e^sink_b). Null means no sink.
  * - Every function returns MLA_OK (0) or a negative status. Host-checkable
  *   problems (null pointers, sizes out of range, unsupported dtypes, a
  *   workspace that is too small) are reported before anything is enqueued.
@@ -241,7 +247,8 @@ int mla_prefill_attention(void* output, const void* q, int32_t dtype,
                           const int32_t* buffer_length_c,
                           int32_t batch_size, int32_t total_q, int32_t num_heads,
                           int32_t max_rows, int32_t max_prompt_len, float scale,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          const float* attn_sink, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * mla_prefill_workspace_size / mla_prefill -- the whole chunked prefill for a
@@ -275,8 +282,8 @@ int mla_prefill(void* output, const void* q, int32_t dtype,
                 const void* freqs_cis, int32_t batch_size, int32_t total_q,
                 int32_t num_heads, int32_t max_prompt_len, int32_t page_size,
                 int32_t max_pages_per_seq, int32_t num_pages, int32_t max_seq_len,
-                float scale, float epsilon, void* workspace, size_t workspace_bytes,
-                hipStream_t stream);
+                float scale, float epsilon, const float* attn_sink, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * mla_decode_workspace_size / mla_decode -- absorbed MLA decode, one new token
@@ -316,7 +323,8 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
                int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
                int32_t max_context_len, int32_t num_partitions, float scale,
-               void* workspace, size_t workspace_bytes, hipStream_t stream);
+               const float* attn_sink, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
 
 /* Text for a status code, and the message of the calling thread's last failure. */
 const char* mla_status_string(int status);
@@ -353,8 +361,8 @@ int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
                       const void* kv_cache, int32_t cache_dtype, const int32_t* d_indices,
                       int32_t indices_stride, const void* w_uk, const void* w_uv,
                       int32_t batch_size, int32_t num_heads, int32_t num_rows, int32_t max_topk,
-                      int32_t num_partitions, float scale, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      int32_t num_partitions, float scale, const float* attn_sink,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -37,16 +37,16 @@ _SIGNATURES = {
     "mla_up_project": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _I, _P]),
     "mla_prefill_attention_workspace_size": (_S, [_I, _I, _I]),
     "mla_prefill_attention": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P,
-                                   _I, _I, _I, _I, _I, _F, _P, _S, _P]),
+                                   _I, _I, _I, _I, _I, _F, _P, _P, _S, _P]),
     "mla_prefill_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_prefill": (_I, [_P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P,
-                         _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, _S, _P]),
+                         _I, _I, _I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _S, _P]),
     "mla_decode_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "mla_decode": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
-                        _P, _S, _P]),
+                        _P, _P, _S, _P]),
     "mla_decode_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_decode_sparse": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F,
-                               _P, _S, _P]),
+                               _P, _P, _S, _P]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -108,6 +108,14 @@ def _dtype_code(t) -> int:
     if t.dtype == torch.float8_e4m3fn:
         return MLA_FP8_E4M3FN
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _sink_ptr(attn_sink, B):
+    """Pointer of an optional float32 [B] tensor of sink logits (None: no sink)."""
+    if attn_sink is None:
+        return None
+    _expect(attn_sink, torch.float32, (B,), "attn_sink")
+    return _ptr(attn_sink)
 
 
 def _expect(t, dtype, shape=None, name="tensor"):
@@ -207,7 +215,8 @@ def mla_prefill_attention_workspace_size(batch_size: int, total_q: int, num_head
 
 def mla_prefill_attention(output, q, k_nope, v_t, krope, input_row_offsets, cache_lengths,
                           buffer_row_offsets_c, cache_offsets_c, buffer_length_c,
-                          max_prompt_len: int, scale: float, workspace, stream=None):
+                          max_prompt_len: int, scale: float, workspace, stream=None,
+                          attn_sink=None):
     Tq, H = q.shape[0], q.shape[1]
     B = cache_lengths.shape[0]
     R = krope.shape[0]
@@ -222,8 +231,8 @@ def mla_prefill_attention(output, q, k_nope, v_t, krope, input_row_offsets, cach
         _ptr(output), _ptr(q), _dtype_code(q), _ptr(k_nope), _ptr(v_t), _ptr(krope),
         _ptr(input_row_offsets), _ptr(cache_lengths), _ptr(buffer_row_offsets_c),
         _ptr(cache_offsets_c), _ptr(buffer_length_c), B, Tq, H, R, int(max_prompt_len),
-        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        float(scale), _sink_ptr(attn_sink, B), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_prefill_attention", st)
 
 
@@ -236,7 +245,7 @@ def mla_prefill_workspace_size(batch_size: int, total_q: int, num_heads: int, ma
 def mla_prefill(output, q, input_row_offsets, cache_lengths, kv_cache, page_table,
                 buffer_row_offsets, cache_offsets, buffer_lengths, max_rows: int, w_k, w_uv,
                 kv_norm_gamma, freqs_cis, max_prompt_len: int, scale: float, epsilon: float,
-                workspace, stream=None):
+                workspace, stream=None, attn_sink=None):
     Tq, H = q.shape[0], q.shape[1]
     B = cache_lengths.shape[0]
     C = buffer_lengths.shape[0]
@@ -253,8 +262,8 @@ def mla_prefill(output, q, input_row_offsets, cache_lengths, kv_cache, page_tabl
         _ptr(buffer_lengths), C, int(max_rows), _ptr(w_k), _ptr(w_uv), _ptr(kv_norm_gamma),
         _ptr(freqs_cis), B, Tq, H, int(max_prompt_len), kv_cache.shape[1],
         page_table.shape[1], kv_cache.shape[0], freqs_cis.shape[0], float(scale),
-        float(epsilon), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream))
+        float(epsilon), _sink_ptr(attn_sink, B), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_prefill", st)
 
 
@@ -266,7 +275,7 @@ def mla_decode_workspace_size(batch_size: int, num_heads: int, max_context_len: 
 
 def mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
                max_context_len: int, scale: float, workspace, num_partitions: int = 0,
-               stream=None):
+               stream=None, attn_sink=None):
     B, H = q.shape[0], q.shape[1]
     _expect(output, torch.bfloat16, (B, H, VD), "output")
     _expect(q, torch.bfloat16, (B, H, QD), "q")
@@ -277,7 +286,8 @@ def mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
         _ptr(output), _ptr(q), _ptr(context_lengths), _ptr(kv_cache), _dtype_code(kv_cache),
         _ptr(page_table), _ptr(w_uk), _ptr(w_uv), B, H, kv_cache.shape[1], page_table.shape[1],
         kv_cache.shape[0], int(max_context_len), int(num_partitions), float(scale),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+        _sink_ptr(attn_sink, B), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
     _check("mla_decode", st)
 
 
@@ -288,7 +298,8 @@ def mla_decode_sparse_workspace_size(batch_size: int, num_heads: int, max_topk: 
 
 
 def mla_decode_sparse(output, q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: int,
-                      scale: float, workspace, num_partitions: int = 0, stream=None):
+                      scale: float, workspace, num_partitions: int = 0, stream=None,
+                      attn_sink=None):
     B, H = q.shape[0], q.shape[1]
     _expect(output, torch.bfloat16, (B, H, VD), "output")
     _expect(q, torch.bfloat16, (B, H, QD), "q")
@@ -303,8 +314,8 @@ def mla_decode_sparse(output, q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, 
     st = load().mla_decode_sparse(
         _ptr(output), _ptr(q), _ptr(topk_lengths), _ptr(kv_cache), _dtype_code(kv_cache),
         _ptr(d_indices), d_indices.shape[1], _ptr(w_uk), _ptr(w_uv), B, H, kv_cache.shape[0],
-        int(max_topk), int(num_partitions), float(scale), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+        int(max_topk), int(num_partitions), float(scale), _sink_ptr(attn_sink, B),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("mla_decode_sparse", st)
 
 
@@ -329,7 +340,7 @@ def plan(input_row_offsets, cache_lengths, buffer_token_size: int, max_chunks: i
 def prefill(q, input_row_offsets, cache_lengths, kv_cache, page_table, w_k, w_uv,
             kv_norm_gamma, freqs_cis, buffer_token_size: int, max_chunks: int,
             max_prompt_len: int, scale: float, epsilon: float, max_rows: int | None = None,
-            workspace=None, output=None, plan_tensors=None, stream=None):
+            workspace=None, output=None, plan_tensors=None, stream=None, attn_sink=None):
     """Plan and run the whole chunked prefill; returns the bf16 output [Tq, H, 128].
 
     max_rows defaults to batch_size * buffer_token_size (always enough)."""
@@ -349,12 +360,13 @@ def prefill(q, input_row_offsets, cache_lengths, kv_cache, page_table, w_k, w_uv
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
     mla_prefill(output, q, input_row_offsets, cache_lengths, kv_cache, page_table, bro, co, bl,
                 max_rows, w_k, w_uv, kv_norm_gamma, freqs_cis, max_prompt_len, scale, epsilon,
-                workspace, stream=stream)
+                workspace, stream=stream, attn_sink=attn_sink)
     return output
 
 
 def decode(q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len: int,
-           scale: float, num_partitions: int = 0, workspace=None, output=None, stream=None):
+           scale: float, num_partitions: int = 0, workspace=None, output=None, stream=None,
+           attn_sink=None):
     """Absorbed decode; returns the bf16 output [B, H, 128]."""
     B, H = q.shape[0], q.shape[1]
     if output is None:
@@ -364,13 +376,14 @@ def decode(q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len
                                            num_partitions, _dtype_code(kv_cache))
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
     mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv, max_context_len,
-               scale, workspace, num_partitions=num_partitions, stream=stream)
+               scale, workspace, num_partitions=num_partitions, stream=stream,
+               attn_sink=attn_sink)
     return output
 
 
 def decode_sparse(q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: int,
                   scale: float, num_partitions: int = 0, workspace=None, output=None,
-                  stream=None):
+                  stream=None, attn_sink=None):
     """Sparse absorbed decode over the listed pool rows; returns [B, H, 128] bf16.
     kv_cache may be given paged ([num_pages, page_size, 576]); it is viewed as rows."""
     B, H = q.shape[0], q.shape[1]
@@ -382,5 +395,6 @@ def decode_sparse(q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: in
                                                   _dtype_code(kv_cache))
         workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
     mla_decode_sparse(output, q, topk_lengths, rows, d_indices, w_uk, w_uv, max_topk, scale,
-                      workspace, num_partitions=num_partitions, stream=stream)
+                      workspace, num_partitions=num_partitions, stream=stream,
+                      attn_sink=attn_sink)
     return output

@@ -304,7 +304,8 @@ static int attention_common(void* output, const void* q, int32_t dtype, const vo
                             const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
                             const uint32_t* bro_c, const uint32_t* co_c, const int32_t* bl_c,
                             int32_t B, int32_t total_q, int32_t H, int32_t max_rows,
-                            float scale, const AttnWs& ws, hipStream_t stream) {
+                            float scale, const float* attn_sink, const AttnWs& ws,
+                            hipStream_t stream) {
   mla::AttnArgs a;
   a.out = (uint16_t*)output;
   a.q = q;
@@ -324,6 +325,7 @@ static int attention_common(void* output, const void* q, int32_t dtype, const vo
   a.H = H;
   a.max_rows = max_rows;
   a.scale_log2 = scale * kLog2e;
+  a.sink = attn_sink;
   return hip_status(mla::launch_prefill_attn(a, dtype == MLA_FP8_E4M3FN, stream),
                     "attention kernel");
 }
@@ -334,7 +336,8 @@ int mla_prefill_attention(void* output, const void* q, int32_t dtype, const void
                           const uint32_t* cache_offsets_c, const int32_t* buffer_length_c,
                           int32_t batch_size, int32_t total_q, int32_t num_heads,
                           int32_t max_rows, int32_t max_prompt_len, float scale,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          const float* attn_sink, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   if (!output || !q || !k_nope || !v_t || !krope || !input_row_offsets || !cache_lengths ||
       !buffer_row_offsets_c || !cache_offsets_c || !buffer_length_c)
     return fail(MLA_ERR_INVALID_ARG, "mla_prefill_attention: null pointer");
@@ -356,8 +359,8 @@ int mla_prefill_attention(void* output, const void* q, int32_t dtype, const void
   if (st != MLA_OK) return st;
   return attention_common(output, q, dtype, k_nope, v_t, krope, input_row_offsets,
                           cache_lengths, buffer_row_offsets_c, cache_offsets_c,
-                          buffer_length_c, batch_size, total_q, num_heads, max_rows, scale, ws,
-                          stream);
+                          buffer_length_c, batch_size, total_q, num_heads, max_rows, scale,
+                          attn_sink, ws, stream);
 }
 
 size_t mla_prefill_workspace_size(int32_t batch_size, int32_t total_q, int32_t num_heads,
@@ -376,6 +379,7 @@ int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* inpu
                 const void* freqs_cis, int32_t batch_size, int32_t total_q, int32_t num_heads,
                 int32_t max_prompt_len, int32_t page_size, int32_t max_pages_per_seq,
                 int32_t num_pages, int32_t max_seq_len, float scale, float epsilon,
+                const float* attn_sink,
                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!output || !q || !input_row_offsets || !cache_lengths || !kv_cache || !page_table ||
       !buffer_row_offsets || !cache_offsets || !buffer_lengths || !w_k || !w_uv ||
@@ -414,7 +418,7 @@ int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* inpu
     if (st != MLA_OK) return st;
     st = attention_common(output, q, dtype, ws.k_nope, ws.v_t, ws.krope, input_row_offsets,
                           cache_lengths, bro_c, co_c, bl_c, batch_size, total_q, num_heads,
-                          rows, scale, ws.attn, stream);
+                          rows, scale, attn_sink, ws.attn, stream);
     if (st != MLA_OK) return st;
   }
   (void)fp8;
@@ -435,7 +439,8 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
                const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
                int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
-               int32_t max_context_len, int32_t num_partitions, float scale, void* workspace,
+               int32_t max_context_len, int32_t num_partitions, float scale,
+               const float* attn_sink, void* workspace,
                size_t workspace_bytes, hipStream_t stream) {
   if (!output || !q || !context_lengths || !kv_cache || !page_table || !w_uk || !w_uv)
     return fail(MLA_ERR_INVALID_ARG, "mla_decode: null pointer");
@@ -502,6 +507,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   c.maxp = max_pages_per_seq;
   c.num_pages = num_pages;
   c.scale_log2 = scale * kLog2e;
+  c.sink = attn_sink;
   c.fp8 = fp8;
   st = hip_status(mla::launch_decode_combine(c, stream), "combine kernel");
   if (st != MLA_OK) return st;
@@ -523,7 +529,8 @@ int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
                       const void* kv_cache, int32_t cache_dtype, const int32_t* d_indices,
                       int32_t indices_stride, const void* w_uk, const void* w_uv,
                       int32_t batch_size, int32_t num_heads, int32_t num_rows, int32_t max_topk,
-                      int32_t num_partitions, float scale, void* workspace,
+                      int32_t num_partitions, float scale, const float* attn_sink,
+                      void* workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   if (!topk_lengths || !d_indices) return fail(MLA_ERR_INVALID_ARG, "mla_decode_sparse: null pointer");
   if (indices_stride < 1 || num_rows < 1 || max_topk < 1 || max_topk > indices_stride)
@@ -531,7 +538,7 @@ int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
                 indices_stride, num_rows, max_topk);
   return mla_decode(output, q, (const uint32_t*)topk_lengths, kv_cache, cache_dtype, d_indices,
                     w_uk, w_uv, batch_size, num_heads, 1, indices_stride, num_rows,
-                    max_topk, num_partitions, scale, workspace,
+                    max_topk, num_partitions, scale, attn_sink, workspace,
                     workspace_bytes, stream);
 }
 

@@ -367,7 +367,11 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   if (!active) return;
   // O^T register i of block md holds dim 32*md + 8*(i/4) + 4*hf + i%4
   if (P < co + len) {  // last visible key is in this chunk: normalise and write
-    const float inv = 1.0f / l_run;
+    // a sink adds e^sink to the denominator (l_run and o are relative to
+    // 2^m_run; no visible key: m_run = -inf, the sink term inf, the output 0)
+    const float l_tot = a.sink ? l_run + __builtin_amdgcn_exp2f(a.sink[b] * 1.44269504088896341f - m_run)
+                               : l_run;
+    const float inv = 1.0f / l_tot;
     uint16_t* op = a.out + (t * a.H + h) * kV;
 #pragma unroll
     for (int md = 0; md < 4; ++md)

@@ -772,6 +772,8 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
         for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt, ow[e], acc[e]);
       }
     }
+    // a sink adds e^sink to the denominator (L and acc are relative to 2^M)
+    if (c.sink) L += __builtin_amdgcn_exp2f(c.sink[b] * 1.44269504088896341f - M);
     const float inv = 1.f / L;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= inv;

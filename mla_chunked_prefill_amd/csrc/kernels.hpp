@@ -51,6 +51,7 @@ struct AttnArgs {
   float* carry_o;
   float* carry_ml;
   const int2* sched;
+  const float* sink;         // [B] sink logits (natural log, scaled-score units), or null
   int n_slots, B, H, max_rows;
   float scale_log2;
 };
@@ -82,6 +83,7 @@ struct CombineArgs {
   const int32_t* page_table;
   int B, H, G, ps, maxp, num_pages;
   float scale_log2;
+  const float* sink;         // [B] sink logits, or null
   bool fp8;                  // cache holds e4m3fn codes (else bf16)
 };
 hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,

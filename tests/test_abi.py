@@ -54,7 +54,7 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert lib.mla_up_project(fake, odd, 0, fake, fake, fake, fake, 2, 128, None) == -1
     assert b"aligned" in lib.mla_last_error()
     assert lib.mla_decode(fake, fake, fake, odd, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
-                          0.1, fake, 1 << 40, None) == -1
+                          0.1, None, fake, 1 << 40, None) == -1
     # KV write: null input, unsupported cache dtype, misaligned cache
     assert lib.mla_kv_write(fake, 0, fake, None, fake, fake, fake, fake, 2, 10, 16, 4, 8, 64,
                             1e-6, None) == -1
@@ -69,20 +69,20 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     need = lib.mla_decode_sparse_workspace_size(4, 8, 100, 0, 0)
     assert need > 0
     assert lib.mla_decode_sparse(fake, fake, fake, fake, 0, fake, 64, fake, fake, 4, 8, 1000, 100,
-                                 0, 0.1, fake, need, None) == -1
+                                 0, 0.1, None, fake, need, None) == -1
     assert lib.mla_decode_sparse(fake, fake, fake, fake, 0, None, 128, fake, fake, 4, 8, 1000, 100,
-                                 0, 0.1, fake, need, None) == -1
+                                 0, 0.1, None, fake, need, None) == -1
     # max_rows not a multiple of 64
     assert lib.mla_up_project(fake, fake, 0, fake, fake, fake, fake, 2, 100, None) == -1
     # workspace too small
     need = lib.mla_decode_workspace_size(4, 8, 1000, 16, 0, 0)
     assert need > 0
     st = lib.mla_decode(fake, fake, fake, fake, 0, fake, fake, fake, 4, 8, 16, 100, 50, 1000, 0,
-                        0.1, fake, need - 1, None)
+                        0.1, None, fake, need - 1, None)
     assert st == -3
     # heads beyond what decode supports
     assert lib.mla_decode(fake, fake, fake, fake, 0, fake, fake, fake, 4, 256, 16, 100, 50, 1000,
-                          0, 0.1, fake, 1 << 40, None) == -1
+                          0, 0.1, None, fake, 1 << 40, None) == -1
 
 
 def test_workspace_sizes_grow_with_problem(lib):

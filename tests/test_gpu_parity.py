@@ -559,3 +559,52 @@ def test_decode_sparse_over_the_context_in_order_equals_decode(B):
         p = np.arange(n)
         idx[b, :n] = wl.page_table[b, p // ps] * ps + p % ps
     _assert_close(_run_sparse(B, wl, idx, ctx), oracle.decode(wl), BF16_MAX, BF16_MEAN)
+
+
+# ---------------------------------------------------------------------------
+# attention sinks: one more logit per sequence in the softmax denominator
+# ---------------------------------------------------------------------------
+
+def _sinks(vals):
+    return torch.tensor(vals, dtype=torch.float32, device="cuda")
+
+
+def test_prefill_sinks_multichunk(B):
+    # sequences split over several chunks: the sink enters once, at the end
+    wl = make_prefill("sink", 44, [70, 5, 140], [0, 60, 9], 2, 16, 64)
+    sinks = [2.5, -np.inf, 0.3]
+    t = prefill_tensors(wl)
+    out = B.prefill(t["q"], t["input_row_offsets"], t["cache_lengths"], t["kv_cache"],
+                    t["page_table"], t["w_k"], t["w_uv"], t["kv_norm_gamma"], t["freqs_cis"],
+                    wl.buffer_token_size, wl.max_chunks, int(wl.new_lens.max()), wl.scale,
+                    wl.eps, attn_sink=_sinks(sinks))
+    torch.cuda.synchronize()
+    _assert_close(_f64(out), oracle.prefill(wl, sinks=np.array(sinks)), BF16_MAX, BF16_MEAN)
+
+
+@pytest.mark.parametrize("parts", [0, 3])
+def test_decode_sinks(B, parts):
+    wl = make_decode("dsk", 53, [1, 37, 300, 64, 1000], 8, 16)
+    sinks = [1.0, 4.0, -np.inf, -3.0, 0.0]
+    t = decode_tensors(wl)
+    out = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
+                   t["w_uv"], int(wl.context_lens.max()), wl.scale, num_partitions=parts,
+                   attn_sink=_sinks(sinks))
+    torch.cuda.synchronize()
+    _assert_close(_f64(out), oracle.decode(wl, sinks=np.array(sinks)), BF16_MAX, BF16_MEAN)
+
+
+def test_decode_sparse_sinks(B):
+    wl = make_decode("spk", 84, [2000, 900, 3000], 16, 16)
+    lens = [5, 300, 0]
+    idx = _sparse_case(wl, lens, 85)
+    sinks = [2.0, -1.0, 5.0]
+    t = decode_tensors(wl)
+    out = B.decode_sparse(t["q"], torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                          t["kv_cache"], torch.from_numpy(idx).cuda(), t["w_uk"], t["w_uv"],
+                          idx.shape[1], wl.scale, attn_sink=_sinks(sinks))
+    torch.cuda.synchronize()
+    dec = oracle.DecodedDecode(wl)
+    ref = oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
+                               dec.nope, dec.lora, sinks=np.array(sinks))
+    _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
