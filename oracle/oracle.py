@@ -35,6 +35,9 @@ Readings where the pages leave a step open (each is listed in the design notes):
 - Query i of sequence b sits at absolute position cache_len[b] + i and sees
   keys at positions p <= cache_len[b] + i.
 - Chunking only bounds memory: the result is attention over all visible keys.
+- The single graph-op call (prefill_decode) writes the new tokens processed,
+  then reads the pool as stored in both branches; max_seq_len counts a
+  sequence's new tokens: above 1 prefill, 1 decode.
 """
 from __future__ import annotations
 
@@ -463,6 +466,65 @@ def decode_sparse(q: np.ndarray, pool: np.ndarray, d_indices: np.ndarray, topk_l
         out[b] = decode_one(q[b], Z, w_uk, w_uv, scale, nope, lora,
                             None if sinks is None else float(sinks[b]))
     return out
+
+
+def prefill_decode(q, input_row_offsets, cache_lengths, pool, page_table, page_size: int,
+                   w_k, w_uk, w_uv, gamma, freqs, scale: float, eps: float, max_seq_len: int,
+                   kv_input=None, d_indices=None, topk_lengths=None, sinks=None,
+                   nope: int = 128, lora: int = 512):
+    """The graph op as one call (mla_prefill_decode_graph_bf16 page:
+    description, the batch's maximum sequence length selects prefill or
+    decode; Parameters "kv_input_fn", "sparse_mla"; Args "max_seq_len",
+    "d_indices", "topk_lengths", "attn_sink_ptr"). Values, not storage bits.
+
+    1. With kv_input (the new tokens' raw rows), every new token is first
+       stored processed in the pool (kv_write).
+    2. max_seq_len > 1, prefill: the queries of sequence b (rows
+       input_row_offsets[b] .. input_row_offsets[b+1] of q, at positions
+       cache_lengths[b] + i) attend causally over the sequence's rows at
+       positions [0, cache_lengths[b] + n_b) read as stored, the latent part
+       up-projected through w_k and w_uv, the rope part shared by all heads.
+       max_seq_len == 1, decode: every sequence brings one token; q row b
+       attends, absorbed through w_uk, over its rows at positions
+       [0, cache_lengths[b] + 1), or with d_indices over the listed pool rows
+       (decode_sparse); the result is projected through w_uv.
+       max_seq_len == 0: no query.
+    The reading: max_seq_len counts a sequence's new tokens (the query
+    length), and both branches read the pool in the processed form the write
+    stores. Returns (output [T_q, H, v], the pool after the write)."""
+    off = np.asarray(input_row_offsets, dtype=np.int64)
+    clen = np.asarray(cache_lengths, dtype=np.int64)
+    B = len(clen)
+    q = np.asarray(q, dtype=np.float64)
+    H = w_uv.shape[0]
+    pool = np.asarray(pool, dtype=np.float64)
+    if kv_input is not None:
+        pool = kv_write(pool, page_table, kv_input, off, clen, gamma, freqs, eps, page_size, lora)
+    out = np.zeros((q.shape[0], H, w_uv.shape[1]))
+    sink = (lambda b: None) if sinks is None else (lambda b: float(sinks[b]))
+    if max_seq_len > 1:
+        for b in range(B):
+            n = int(off[b + 1] - off[b])
+            if n == 0:
+                continue
+            L = int(clen[b]) + n
+            rows = gather_rows(pool, page_table, b, np.arange(L), page_size)
+            k_nope, v = up_project(rows[:, :lora], w_k, w_uv, H)
+            qpos = clen[b] + np.arange(n)
+            out[off[b]:off[b + 1]] = attend_sequence(q[off[b]:off[b + 1]], k_nope,
+                                                     rows[:, lora:], v, qpos, np.arange(L),
+                                                     scale, nope, sink(b))
+    elif max_seq_len == 1:
+        if np.any(off[1:] - off[:-1] != 1):
+            raise ValueError("decode takes exactly one new token per sequence")
+        if d_indices is not None:
+            out[:] = decode_sparse(q, pool, d_indices, topk_lengths, w_uk, w_uv, scale, nope,
+                                   lora, sinks)
+        else:
+            for b in range(B):
+                Z = gather_rows(pool, page_table, b, np.arange(int(clen[b]) + 1), page_size)
+                out[b] = decode_one(q[b], Z, w_uk, w_uv, scale, nope, lora, sink(b))
+    return out, pool
 
 
 def decode_split(wl, num_splits: int, dec: DecodedDecode | None = None) -> np.ndarray:

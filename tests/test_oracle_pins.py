@@ -529,3 +529,82 @@ def test_decode_sink_with_zero_query_closed_form():
         Z = oracle.gather_rows(ddec.pool, dwl.page_table, b, np.arange(n), dwl.page_size)
         olat = Z[:, :ddec.lora].sum(axis=0) / (n + math.exp(sinks[b]))
         assert np.allclose(out[b], np.einsum("hdl,l->hd", ddec.w_uv, olat), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the graph op as one call: write, then prefill or decode by max_seq_len
+# ---------------------------------------------------------------------------
+
+def _unified_inputs(wl):
+    """Values of a prefill workload, the pool holding every position's row
+    processed (written by kv_write from the raw rows, position by position)."""
+    dec = oracle.Decoded(wl)
+    lens = [dec.clen[b] + dec.offs[b + 1] - dec.offs[b] for b in range(dec.B)]
+    raw = np.concatenate([oracle.gather_rows(dec.pool, wl.page_table, b, np.arange(n),
+                                             wl.page_size) for b, n in enumerate(lens)])
+    offs = np.concatenate([[0], np.cumsum(lens)])
+    done = oracle.kv_write(np.zeros_like(dec.pool), wl.page_table, raw, offs, np.zeros(dec.B),
+                           dec.gamma, dec.freqs, wl.eps, wl.page_size, dec.lora)
+    return dec, raw, offs, done
+
+
+def _unified(wl, dec, pool, max_seq_len, **kw):
+    return oracle.prefill_decode(dec.q, dec.offs, dec.clen, pool, wl.page_table, wl.page_size,
+                                 dec.w_k, dec.w_uk, dec.w_uv, dec.gamma, dec.freqs, wl.scale,
+                                 wl.eps, max_seq_len, nope=dec.nope, lora=dec.lora, **kw)
+
+
+def test_unified_prefill_over_the_written_cache_is_prefill_over_raw_rows():
+    wl = _tiny_prefill(41, [3, 5, 2], [4, 0, 6], H=3)
+    dec, raw, offs, done = _unified_inputs(wl)
+    ref = oracle.prefill(wl, dec)
+    got, pool = _unified(wl, dec, done, 5)
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-13)
+    assert np.array_equal(pool, done)
+    # the call itself writing the new tokens: only the cached positions are in
+    # the pool beforehand, the new tokens' raw rows come in as kv_input
+    cached_only = done.copy()
+    flat = cached_only.reshape(-1, cached_only.shape[-1])
+    new_rows = []
+    for b in range(dec.B):
+        p = dec.clen[b] + np.arange(dec.offs[b + 1] - dec.offs[b])
+        flat[wl.page_table[b, p // wl.page_size].astype(np.int64) * wl.page_size
+             + p % wl.page_size] = 7.0            # stale values the write must replace
+        new_rows.append(raw[offs[b] + p])
+    got2, pool2 = _unified(wl, dec, cached_only, 5, kv_input=np.concatenate(new_rows))
+    assert np.allclose(got2, ref, rtol=1e-11, atol=1e-13)
+    assert np.allclose(pool2, done, rtol=1e-15, atol=0)
+
+
+def test_unified_decode_branch_equals_the_prefill_branch_for_one_token():
+    # absorption: with w_uk[h] = w_k[h]^T the absorbed decode of one new token
+    # equals the up-projected prefill of the same token
+    wl = _tiny_prefill(42, [1, 1, 1], [4, 0, 9], H=3)
+    dec, raw, offs, done = _unified_inputs(wl)
+    dec.w_uk = dec.w_k.reshape(dec.H, dec.nope, dec.lora).transpose(0, 2, 1).copy()
+    a, _ = _unified(wl, dec, done, 1)
+    b, _ = _unified(wl, dec, done, 2)
+    assert np.allclose(a, b, rtol=1e-10, atol=1e-12)
+    assert np.allclose(a, oracle.prefill(wl, dec), rtol=1e-10, atol=1e-12)
+    # sparse over every context row in order is the dense decode branch
+    idx = np.full((dec.B, 12), -1, dtype=np.int32)
+    for bb in range(dec.B):
+        p = np.arange(dec.clen[bb] + 1)
+        idx[bb, :len(p)] = wl.page_table[bb, p // wl.page_size] * wl.page_size + p % wl.page_size
+    c, _ = _unified(wl, dec, done, 1, d_indices=idx,
+                    topk_lengths=[dec.clen[bb] + 1 for bb in range(dec.B)])
+    assert np.allclose(c, a, rtol=1e-12, atol=1e-14)
+    # sinks pass through to the branch
+    s = np.array([0.5, -1.0, 2.0])
+    d1, _ = _unified(wl, dec, done, 1, sinks=s)
+    d2, _ = _unified(wl, dec, done, 2, sinks=s)
+    assert np.allclose(d1, d2, rtol=1e-10, atol=1e-12) and not np.allclose(d1, a)
+
+
+def test_unified_decode_rejects_ragged_batches_and_zero_length_is_empty():
+    wl = _tiny_prefill(43, [2, 1], [3, 1], H=2)
+    dec, raw, offs, done = _unified_inputs(wl)
+    with pytest.raises(ValueError):
+        _unified(wl, dec, done, 1)
+    got, pool = _unified(wl, dec, done, 0)
+    assert np.array_equal(got, np.zeros_like(got)) and np.array_equal(pool, done)
