@@ -12,8 +12,12 @@ per-call durations; the attention call is the dominant kernel.
 A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
 batch (contexts U{4096..32768}), with a bf16 and then an e4m3 cache, and
 reports achieved HBM bandwidth, then mla_decode_sparse with every sequence
-listing 2048 rows of its context. A last phase times mla_kv_write storing the
-prompt's 4096 new tokens into the paged cache (normalised, rotated).
+listing 2048 rows of its context. Then mla_kv_write stores the prompt's 4096
+new tokens into the paged cache (normalised, rotated; timed as HIP graph
+replays, the launches being shorter than the host's issue time), and
+mla_prefill_decode runs the graph op as one call in its prefill branch (write
++ prefill over stored rows) and its decode branch (write + decode, also as
+graph replays).
 
 Before the W warm-up steps, about S seconds (default 1) of the same work run
 untimed, so that the GPU clock has left its idle state; the K timed steps are
@@ -80,6 +84,42 @@ def warm_clock(fn, seconds: float, torch):
         for _ in range(4):
             fn()
         torch.cuda.synchronize()
+
+
+def graph_ms(fn, per_graph: int, reps: int, torch):
+    """Capture per_graph back-to-back calls of fn into one HIP graph, replay
+    it reps times between two events; returns ms per call. For calls whose
+    kernels take less time than the host needs to launch them."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * per_graph)
+
+
+def event_ms(fn, steps: int, torch):
+    """Mean duration of fn between two events on the current stream."""
+    evs = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
 def bench_prefill(args, binding, torch):
@@ -251,8 +291,9 @@ def bench_decode_sparse(args, binding, torch, topk=2048):
 def bench_kv_write(args, binding, torch):
     """mla_kv_write on the prompt of dsv3_prefill_4k: 4096 new tokens' raw
     576-wide rows normalised, rotated and stored in a bf16 pool of 128-row
-    pages (shuffled page table). A launch takes microseconds, so calls are
-    timed in groups of 20 between events."""
+    pages (shuffled page table). A launch takes microseconds, less than the
+    host needs to issue it, so 20 calls are captured into a HIP graph whose
+    replays are timed."""
     import numpy as np
     from workloads import f32_to_bf16_bits
     from workloads.gen import rope_table_bits
@@ -275,20 +316,87 @@ def bench_kv_write(args, binding, torch):
         binding.mla_kv_write(cache, pt, x, offs, clen, gamma, freqs, 1e-6)
 
     warm_clock(call, args.warm_seconds / 4, torch)
-    group = 20
-    evs = []
-    for _ in range(max(1, args.steps // 4)):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(group):
-            call()
-        e1.record()
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / (len(evs) * group)
+    ms = graph_ms(call, 20, max(1, args.steps // 2), torch)
     bytes_alg = n * (576 * 2 + 576 * 2 + 64 * 2) + 512 * 2
     return dict(ms=ms, bytes=bytes_alg)
+
+
+def bench_unified(args, binding, torch):
+    """mla_prefill_decode, the graph op as one call, in both branches:
+    prefill: dsv3_prefill_4k's prompt arrives as 4096 raw rows (kv_input),
+    is written into the pool, and the planned prefill reads every row as
+    stored; decode: decode_b64's 64 new tokens arrive raw, are written, and
+    each sequence attends over its cache_len + 1 rows. The decode call is
+    also timed as a replay of a captured HIP graph."""
+    import numpy as np
+    from workloads import decode_recipe, f32_to_bf16_bits, prefill_recipe
+    from workloads.device import decode_tensors, prefill_tensors
+    from workloads.gen import rope_table_bits
+
+    rng = np.random.default_rng(11)
+
+    def bf(a):
+        return torch.from_numpy(f32_to_bf16_bits(a.astype(np.float32)).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    gamma = bf(1.0 + 0.1 * rng.standard_normal(512))
+    res = {}
+
+    wl = prefill_recipe("dsv3_prefill_4k")
+    t = prefill_tensors(wl)
+    Bp, H, T, C, Tq = wl.batch, wl.num_heads, wl.buffer_token_size, wl.max_chunks, wl.total_q
+    x = bf(rng.standard_normal((Tq, 576)))
+    max_rows = (min(Bp * T, int(sum(min(int(L), T) for L in wl.seq_lens))) + 63) // 64 * 64
+    plan_t = binding.plan(t["input_row_offsets"], t["cache_lengths"], T, C)
+    max_new, max_cache = int(wl.new_lens.max()), int(wl.cached_lens.max())
+    ws = torch.empty(binding.mla_prefill_decode_workspace_size(
+        Bp, Tq, H, max_new, max_rows, max_cache, wl.page_size, 0, 0, binding.MLA_BF16),
+        dtype=torch.uint8, device="cuda")
+    out = torch.empty((Tq, H, 128), dtype=torch.bfloat16, device="cuda")
+
+    def pcall():
+        binding.mla_prefill_decode(out, t["q"], t["input_row_offsets"], t["cache_lengths"],
+                                   t["kv_cache"], t["page_table"], t["w_uk"], t["w_uv"], gamma,
+                                   t["freqs_cis"], max_new, max_cache, wl.scale, wl.eps, ws,
+                                   kv_input=x, w_k=t["w_k"], plan_tensors=plan_t,
+                                   max_rows=max_rows)
+
+    warm_clock(pcall, args.warm_seconds / 2, torch)
+    for _ in range(args.warmup):
+        pcall()
+    torch.cuda.synchronize()
+    res["prefill_ms"] = event_ms(pcall, args.steps, torch)
+    del t, ws, out
+
+    dl = decode_recipe("decode_b64")
+    d = decode_tensors(dl)
+    Bd = dl.batch
+    ctx = dl.context_lens.astype(np.int64)
+    xd = bf(rng.standard_normal((Bd, 576)))
+    freqs = torch.from_numpy(rope_table_bits(int(ctx.max()), 64).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    offs = torch.arange(Bd + 1, dtype=torch.int64).to(torch.uint32).cuda()
+    clen = torch.from_numpy((ctx - 1).astype(np.uint32)).cuda()
+    max_cache = int(ctx.max()) - 1
+    wsd = torch.empty(binding.mla_prefill_decode_workspace_size(
+        Bd, Bd, dl.num_heads, 1, 0, max_cache, dl.page_size, 0, 0, binding.MLA_BF16),
+        dtype=torch.uint8, device="cuda")
+    outd = torch.empty((Bd, dl.num_heads, 128), dtype=torch.bfloat16, device="cuda")
+
+    def dcall():
+        binding.mla_prefill_decode(outd, d["q"], offs, clen, d["kv_cache"], d["page_table"],
+                                   d["w_uk"], d["w_uv"], gamma, freqs, 1, max_cache, dl.scale,
+                                   1e-6, wsd, kv_input=xd)
+
+    warm_clock(dcall, args.warm_seconds / 2, torch)
+    for _ in range(args.warmup):
+        dcall()
+    torch.cuda.synchronize()
+    res["decode_ms"] = event_ms(dcall, args.steps, torch)
+    res["decode_graph_ms"] = graph_ms(dcall, 4, max(1, args.steps // 2), torch)
+    res["decode_bytes"] = (int(ctx.sum()) * 576 * 2 + 2 * dl.num_heads * 512 * 128 * 2 +
+                           Bd * dl.num_heads * (192 + 128) * 2 + Bd * (576 * 2 + 576 * 2))
+    return res
 
 
 def cpu_baseline(full_wl, heads: int):
@@ -438,6 +546,21 @@ def main():
         "frac": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes": kw["bytes"],
     }
+    if not args.no_decode:
+        un = bench_unified(args, binding, torch)
+        gbps = un["decode_bytes"] / (un["decode_ms"] * 1e-3) / 1e9
+        line["prefill_decode"] = {
+            "workload": "mla_prefill_decode, the graph op as one call: prefill branch on "
+                        "dsv3_prefill_4k with its 4096 raw rows written first and every row "
+                        "read as stored; decode branch on decode_b64 with each new token's "
+                        "raw row written first",
+            "prefill_ms": round(un["prefill_ms"], 4),
+            "prefill_attn_tflops": round(p["attn_flop"] / (un["prefill_ms"] * 1e-3) / 1e12, 2),
+            "decode_ms": round(un["decode_ms"], 4),
+            "decode_graph_replay_ms": round(un["decode_graph_ms"], 4),
+            "decode_achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "decode_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        }
     if not args.no_cpu:
         tf, sec, threads = cpu_baseline(p["wl"], args.cpu_heads)
         line["cpu_baseline"] = {

@@ -33,7 +33,7 @@
  *   "bf16" is bfloat16, "e4m3" is OCP float8_e4m3fn (1-4-3, bias 7, no
  *   infinities), each passed as raw storage.
  * - Attention sinks ("mla_prefill_decode_graph_bf16" page, Args
- *   "attn_sink_ptr": optional per-batch attention sink weights): the
+ *   "attn_sink_ptr", an optional float32 sink per batch entry): the
  *   attention entry points take attn_sink, float32 [batch_size] or null. A
  *   sequence's sink is one more logit, in the units of the scaled scores, in
  *   the softmax denominator with a zero value vector: weights become
@@ -363,6 +363,65 @@ int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
                       int32_t batch_size, int32_t num_heads, int32_t num_rows, int32_t max_topk,
                       int32_t num_partitions, float scale, const float* attn_sink,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mla_prefill_decode_workspace_size / mla_prefill_decode -- the graph op as
+ * one call ("mla_prefill_decode_graph_bf16" page: description, prefill or
+ * decode chosen by the batch's maximum sequence length; Parameters
+ * "kv_input_fn", "sparse_mla"; Args "max_seq_len", "d_indices",
+ * "indices_stride", "topk_lengths", "attn_sink_ptr", "num_partitions_in").
+ *
+ * Steps, in stream order:
+ *  1. kv_input not null: the new tokens' raw rows are stored normalised and
+ *     rotated in their paged slots (mla_kv_write with total_q tokens and
+ *     freqs_len table rows).
+ *  2. max_seq_len > 1 -- prefill: the planned chunk loop of mla_prefill, but
+ *     every pool row (cached and new) is read as stored, already normalised
+ *     and rotated, the form step 1 writes; gamma and freqs_cis are not read
+ *     by this step. q is bf16.
+ *     max_seq_len == 1 -- decode: every sequence brings exactly one token
+ *     (total_q must equal batch_size); q row b attends over the sequence's
+ *     cache_lengths[b] + 1 rows (the cached ones and the new one) as
+ *     mla_decode does, or, when d_indices is not null, over its listed rows
+ *     as mla_decode_sparse does (max_topk = indices_stride, the pool viewed
+ *     as num_pages * page_size rows).
+ *     max_seq_len == 0 -- no query (total_q must be 0); only step 1 runs.
+ *
+ *   max_seq_len: host value, the largest number of new tokens of any
+ *     sequence in the batch; it picks the branch.
+ *   max_cache_len: host upper bound on every cache_lengths[b] (decode).
+ *   buffer_row_offsets, cache_offsets, buffer_lengths, max_chunks, max_rows:
+ *     the plan, as mla_prefill (prefill only; may be null for decode).
+ *   w_k (prefill), w_uk (decode), w_uv (both); kv_norm_gamma and freqs_cis
+ *     [freqs_len, 64] are read only by step 1.
+ *   d_indices, indices_stride, topk_lengths: sparse decode, or null / 0.
+ *   attn_sink: float32 [batch_size] or null, in either branch.
+ *   num_partitions: split-KV workgroups of the decode branch, 0 = one per
+ *     compute unit. It and every grid are host values, so the call can be
+ *     captured into a HIP graph and replayed with new device data.
+ * Other arguments as mla_kv_write, mla_prefill and mla_decode. The workspace
+ * holds at least mla_prefill_decode_workspace_size(...) bytes for the branch
+ * max_seq_len selects (indices_stride 0 for dense decode).
+ */
+size_t mla_prefill_decode_workspace_size(int32_t batch_size, int32_t total_q,
+                                         int32_t num_heads, int32_t max_seq_len,
+                                         int32_t max_rows, int32_t max_cache_len,
+                                         int32_t page_size, int32_t indices_stride,
+                                         int32_t num_partitions, int32_t cache_dtype);
+int mla_prefill_decode(void* output, const void* q, const void* kv_input,
+                       const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                       void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                       const uint32_t* buffer_row_offsets, const uint32_t* cache_offsets,
+                       const int32_t* buffer_lengths, int32_t max_chunks, int32_t max_rows,
+                       const void* w_k, const void* w_uk, const void* w_uv,
+                       const void* kv_norm_gamma, const void* freqs_cis, int32_t batch_size,
+                       int32_t total_q, int32_t num_heads, int32_t max_seq_len,
+                       int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                       int32_t max_cache_len, int32_t freqs_len, float scale, float epsilon,
+                       const int32_t* d_indices, int32_t indices_stride,
+                       const int32_t* topk_lengths, const float* attn_sink,
+                       int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

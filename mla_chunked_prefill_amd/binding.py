@@ -47,6 +47,10 @@ _SIGNATURES = {
     "mla_decode_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_decode_sparse": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F,
                                _P, _P, _S, _P]),
+    "mla_prefill_decode_workspace_size": (_S, [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]),
+    "mla_prefill_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I,
+                                _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                _F, _F, _P, _I, _P, _P, _I, _P, _S, _P]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -319,6 +323,74 @@ def mla_decode_sparse(output, q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, 
     _check("mla_decode_sparse", st)
 
 
+def mla_prefill_decode_workspace_size(batch_size: int, total_q: int, num_heads: int,
+                                      max_seq_len: int, max_rows: int, max_cache_len: int,
+                                      page_size: int, indices_stride: int, num_partitions: int,
+                                      cache_dtype: int) -> int:
+    return int(load().mla_prefill_decode_workspace_size(
+        batch_size, total_q, num_heads, max_seq_len, max_rows, max_cache_len, page_size,
+        indices_stride, num_partitions, cache_dtype))
+
+
+def mla_prefill_decode(output, q, input_row_offsets, cache_lengths, kv_cache, page_table,
+                       w_uk, w_uv, kv_norm_gamma, freqs_cis, max_seq_len: int,
+                       max_cache_len: int, scale: float, epsilon: float, workspace,
+                       kv_input=None, w_k=None, plan_tensors=None, max_rows: int = 0,
+                       d_indices=None, topk_lengths=None, attn_sink=None,
+                       num_partitions: int = 0, stream=None):
+    """The graph op as one call: optional KV write of kv_input, then prefill
+    (max_seq_len > 1, plan_tensors = (buffer_row_offsets, cache_offsets,
+    buffer_lengths) and w_k needed) or decode (max_seq_len == 1; sparse when
+    d_indices is given) over the pool as stored."""
+    Tq = q.shape[0]
+    B = cache_lengths.shape[0]
+    H = w_uv.shape[0]
+    _expect(output, torch.bfloat16, (Tq, H, VD), "output")
+    _expect(q, torch.bfloat16, (Tq, H, QD), "q")
+    _expect(input_row_offsets, torch.uint32, (B + 1,), "input_row_offsets")
+    _expect(cache_lengths, torch.uint32, (B,), "cache_lengths")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != CACHE:
+        raise ValueError("kv_cache shape")
+    _expect(page_table, torch.int32, None, "page_table")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table shape")
+    _expect(w_uv, torch.bfloat16, (H, VD, LORA), "w_uv")
+    if w_uk is not None:
+        _expect(w_uk, torch.bfloat16, (H, LORA, NOPE), "w_uk")
+    if w_k is not None:
+        _expect(w_k, torch.bfloat16, (H * NOPE, LORA), "w_k")
+    _expect(kv_norm_gamma, torch.bfloat16, (LORA,), "kv_norm_gamma")
+    _expect(freqs_cis, torch.bfloat16, (freqs_cis.shape[0], ROPE), "freqs_cis")
+    if kv_input is not None:
+        _expect(kv_input, torch.bfloat16, (Tq, CACHE), "kv_input")
+    bro = co = bl = None
+    C = 0
+    if plan_tensors is not None:
+        bro, co, bl = plan_tensors[:3]
+        C = bl.shape[0]
+        _expect(bro, torch.uint32, (C, B + 1), "buffer_row_offsets")
+        _expect(co, torch.uint32, (C, B), "cache_offsets")
+        _expect(bl, torch.int32, (C,), "buffer_lengths")
+    stride = 0
+    if d_indices is not None:
+        _expect(d_indices, torch.int32, None, "d_indices")
+        if d_indices.dim() != 2 or d_indices.shape[0] != B:
+            raise ValueError("d_indices shape")
+        _expect(topk_lengths, torch.int32, (B,), "topk_lengths")
+        stride = d_indices.shape[1]
+    st = load().mla_prefill_decode(
+        _ptr(output), _ptr(q), _ptr(kv_input), _ptr(input_row_offsets), _ptr(cache_lengths),
+        _ptr(kv_cache), _dtype_code(kv_cache), _ptr(page_table), _ptr(bro), _ptr(co), _ptr(bl),
+        C, int(max_rows), _ptr(w_k), _ptr(w_uk), _ptr(w_uv), _ptr(kv_norm_gamma),
+        _ptr(freqs_cis), B, Tq, H, int(max_seq_len), kv_cache.shape[1], page_table.shape[1],
+        kv_cache.shape[0], int(max_cache_len), freqs_cis.shape[0], float(scale),
+        float(epsilon), _ptr(d_indices), stride, _ptr(topk_lengths), _sink_ptr(attn_sink, B),
+        int(num_partitions), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("mla_prefill_decode", st)
+
+
 # ---------------------------------------------------------------------------
 # convenience: plan + workspace + call
 # ---------------------------------------------------------------------------
@@ -397,4 +469,41 @@ def decode_sparse(q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: in
     mla_decode_sparse(output, q, topk_lengths, rows, d_indices, w_uk, w_uv, max_topk, scale,
                       workspace, num_partitions=num_partitions, stream=stream,
                       attn_sink=attn_sink)
+    return output
+
+
+def prefill_decode(q, input_row_offsets, cache_lengths, kv_cache, page_table, w_uk, w_uv,
+                   kv_norm_gamma, freqs_cis, max_seq_len: int, max_cache_len: int,
+                   scale: float, epsilon: float, kv_input=None, w_k=None,
+                   buffer_token_size: int = 8192, max_chunks: int = 1,
+                   max_rows: int | None = None, d_indices=None, topk_lengths=None,
+                   attn_sink=None, num_partitions: int = 0, workspace=None, output=None,
+                   plan_tensors=None, stream=None):
+    """The graph op as one call (plans the chunks for a prefill); returns the
+    bf16 output [total_q, H, 128]."""
+    B = cache_lengths.shape[0]
+    Tq, H = q.shape[0], w_uv.shape[0]
+    if max_seq_len > 1:
+        if max_rows is None:
+            max_rows = B * int(buffer_token_size)
+        max_rows = (int(max_rows) + 63) // 64 * 64
+        if plan_tensors is None:
+            plan_tensors = plan(input_row_offsets, cache_lengths, buffer_token_size,
+                                max_chunks, stream)
+    else:
+        max_rows = 0
+    stride = 0 if d_indices is None else d_indices.shape[1]
+    if output is None:
+        output = torch.empty((Tq, H, VD), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        nbytes = mla_prefill_decode_workspace_size(B, Tq, H, max_seq_len, max_rows,
+                                                   max_cache_len, kv_cache.shape[1], stride,
+                                                   num_partitions, _dtype_code(kv_cache))
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=q.device)
+    mla_prefill_decode(output, q, input_row_offsets, cache_lengths, kv_cache, page_table, w_uk,
+                       w_uv, kv_norm_gamma, freqs_cis, max_seq_len, max_cache_len, scale,
+                       epsilon, workspace, kv_input=kv_input, w_k=w_k,
+                       plan_tensors=plan_tensors, max_rows=max_rows, d_indices=d_indices,
+                       topk_lengths=topk_lengths, attn_sink=attn_sink,
+                       num_partitions=num_partitions, stream=stream)
     return output

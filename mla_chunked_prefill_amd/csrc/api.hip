@@ -159,6 +159,36 @@ DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
   return w;
 }
 
+// One chunk's rows into the contiguous buffers (no argument checks). processed:
+// the pool rows are copied as stored; otherwise they are normalised and rotated.
+int gather_rows(void* latent_out, void* krope_out, int32_t krope_dtype, const void* kv_cache,
+                int32_t cache_dtype, bool processed, const int32_t* page_table,
+                const uint32_t* bro_c, const uint32_t* co_c, const int32_t* bl_c,
+                const void* gamma, const void* freqs, int32_t B, int32_t page_size,
+                int32_t maxp, int32_t num_pages, int32_t max_rows, int32_t freqs_len, float eps,
+                hipStream_t stream) {
+  mla::GatherArgs a;
+  a.latn = (uint16_t*)latent_out;
+  a.krope = krope_out;
+  a.cache = kv_cache;
+  a.page_table = page_table;
+  a.bro_c = bro_c;
+  a.co_c = co_c;
+  a.bl_c = bl_c;
+  a.gamma = (const uint16_t*)gamma;
+  a.freqs = (const uint16_t*)freqs;
+  a.B = B;
+  a.ps = page_size;
+  a.maxp = maxp;
+  a.num_pages = num_pages;
+  a.max_rows = max_rows;
+  a.max_seq_len = freqs_len;
+  a.eps = eps;
+  return hip_status(mla::launch_gather(a, cache_dtype == MLA_FP8_E4M3FN,
+                                       krope_dtype == MLA_FP8_E4M3FN, processed, stream),
+                    "gather kernel");
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,27 +242,18 @@ int mla_gather_norm_rope(void* latent_out, void* krope_out, int32_t krope_dtype,
   if (batch_size < 1 || page_size < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
       max_rows < 1 || max_seq_len < 1 || !(epsilon >= 0.f))
     return fail(MLA_ERR_INVALID_ARG, "mla_gather_norm_rope: sizes");
-  mla::GatherArgs a;
-  a.latn = (uint16_t*)latent_out;
-  a.krope = krope_out;
-  a.cache = kv_cache;
-  a.page_table = page_table;
-  a.bro_c = buffer_row_offsets_c;
-  a.co_c = cache_offsets_c;
-  a.bl_c = buffer_length_c;
-  a.gamma = (const uint16_t*)kv_norm_gamma;
-  a.freqs = (const uint16_t*)freqs_cis;
-  a.B = batch_size;
-  a.ps = page_size;
-  a.maxp = max_pages_per_seq;
-  a.num_pages = num_pages;
-  a.max_rows = max_rows;
-  a.max_seq_len = max_seq_len;
-  a.eps = epsilon;
-  return hip_status(mla::launch_gather(a, cache_dtype == MLA_FP8_E4M3FN,
-                                       krope_dtype == MLA_FP8_E4M3FN, stream),
-                    "gather kernel");
+  return gather_rows(latent_out, krope_out, krope_dtype, kv_cache, cache_dtype, false,
+                     page_table, buffer_row_offsets_c, cache_offsets_c, buffer_length_c,
+                     kv_norm_gamma, freqs_cis, batch_size, page_size, max_pages_per_seq,
+                     num_pages, max_rows, max_seq_len, epsilon, stream);
 }
+
+static int kv_write_rows(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                         const void* kv_input, const uint32_t* input_row_offsets,
+                         const uint32_t* cache_lengths, const void* kv_norm_gamma,
+                         const void* freqs_cis, int32_t batch_size, int32_t total_tokens,
+                         int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                         int32_t max_seq_len, float epsilon, hipStream_t stream);
 
 int mla_kv_write(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
                  const void* kv_input, const uint32_t* input_row_offsets,
@@ -249,6 +270,18 @@ int mla_kv_write(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
   if (batch_size < 1 || total_tokens < 0 || page_size < 1 || max_pages_per_seq < 1 ||
       num_pages < 1 || max_seq_len < 1 || !(epsilon >= 0.f))
     return fail(MLA_ERR_INVALID_ARG, "mla_kv_write: sizes");
+  return kv_write_rows(kv_cache, cache_dtype, page_table, kv_input, input_row_offsets,
+                       cache_lengths, kv_norm_gamma, freqs_cis, batch_size, total_tokens,
+                       page_size, max_pages_per_seq, num_pages, max_seq_len, epsilon, stream);
+}
+
+// The KV write launch (arguments already checked).
+static int kv_write_rows(void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                         const void* kv_input, const uint32_t* input_row_offsets,
+                         const uint32_t* cache_lengths, const void* kv_norm_gamma,
+                         const void* freqs_cis, int32_t batch_size, int32_t total_tokens,
+                         int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                         int32_t max_seq_len, float epsilon, hipStream_t stream) {
   if (total_tokens == 0) return MLA_OK;
   mla::KvWriteArgs a;
   a.cache = kv_cache;
@@ -363,6 +396,46 @@ int mla_prefill_attention(void* output, const void* q, int32_t dtype, const void
                           attn_sink, ws, stream);
 }
 
+// The chunk loop of a planned prefill (arguments already checked; rows is
+// max_rows rounded up to 64): per chunk gather, up-projection, attention with
+// the carried softmax state. Chunks whose buffer length is -1 exit on the device.
+static int prefill_chunks(void* output, const void* q, int32_t dtype,
+                          const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                          const void* kv_cache, int32_t cache_dtype, bool processed,
+                          const int32_t* page_table, const uint32_t* buffer_row_offsets,
+                          const uint32_t* cache_offsets, const int32_t* buffer_lengths,
+                          int32_t max_chunks, int32_t rows, const void* w_k, const void* w_uv,
+                          const void* kv_norm_gamma, const void* freqs_cis, int32_t batch_size,
+                          int32_t total_q, int32_t num_heads, int32_t page_size,
+                          int32_t max_pages_per_seq, int32_t num_pages, int32_t freqs_len,
+                          float scale, float epsilon, const float* attn_sink, void* workspace,
+                          hipStream_t stream) {
+  PrefillWs ws =
+      prefill_ws_layout((char*)workspace, batch_size, total_q, num_heads, rows, dtype);
+  int st = hip_status(mla::launch_attn_schedule(ws.attn.sched, input_row_offsets, batch_size,
+                                                mla::attn_num_slots(batch_size, total_q),
+                                                stream),
+                      "schedule kernel");
+  if (st != MLA_OK) return st;
+  for (int c = 0; c < max_chunks; ++c) {
+    const uint32_t* bro_c = buffer_row_offsets + (size_t)c * (batch_size + 1);
+    const uint32_t* co_c = cache_offsets + (size_t)c * batch_size;
+    const int32_t* bl_c = buffer_lengths + c;
+    st = gather_rows(ws.latn, ws.krope, dtype, kv_cache, cache_dtype, processed, page_table,
+                     bro_c, co_c, bl_c, kv_norm_gamma, freqs_cis, batch_size, page_size,
+                     max_pages_per_seq, num_pages, rows, freqs_len, epsilon, stream);
+    if (st != MLA_OK) return st;
+    st = mla_up_project(ws.k_nope, ws.v_t, dtype, ws.latn, w_k, w_uv, bl_c, num_heads, rows,
+                        stream);
+    if (st != MLA_OK) return st;
+    st = attention_common(output, q, dtype, ws.k_nope, ws.v_t, ws.krope, input_row_offsets,
+                          cache_lengths, bro_c, co_c, bl_c, batch_size, total_q, num_heads,
+                          rows, scale, attn_sink, ws.attn, stream);
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
+}
+
 size_t mla_prefill_workspace_size(int32_t batch_size, int32_t total_q, int32_t num_heads,
                                   int32_t max_rows, int32_t dtype) {
   if (batch_size < 1 || total_q < 0 || num_heads < 1 || max_rows < 1 || !dtype_ok(dtype))
@@ -397,33 +470,20 @@ int mla_prefill(void* output, const void* q, int32_t dtype, const uint32_t* inpu
       mla_prefill_workspace_size(batch_size, total_q, num_heads, max_rows, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "mla_prefill: workspace %zu < %zu", workspace_bytes, need);
-  PrefillWs ws =
-      prefill_ws_layout((char*)workspace, batch_size, total_q, num_heads, rows, dtype);
-  const bool fp8 = dtype == MLA_FP8_E4M3FN;
-  int st = hip_status(mla::launch_attn_schedule(ws.attn.sched, input_row_offsets, batch_size,
-                                                mla::attn_num_slots(batch_size, total_q),
-                                                stream),
-                      "schedule kernel");
-  if (st != MLA_OK) return st;
-  for (int c = 0; c < max_chunks; ++c) {
-    const uint32_t* bro_c = buffer_row_offsets + (size_t)c * (batch_size + 1);
-    const uint32_t* co_c = cache_offsets + (size_t)c * batch_size;
-    const int32_t* bl_c = buffer_lengths + c;
-    st = mla_gather_norm_rope(ws.latn, ws.krope, dtype, kv_cache, dtype, page_table, bro_c,
-                              co_c, bl_c, kv_norm_gamma, freqs_cis, batch_size, page_size,
-                              max_pages_per_seq, num_pages, rows, max_seq_len, epsilon, stream);
-    if (st != MLA_OK) return st;
-    st = mla_up_project(ws.k_nope, ws.v_t, dtype, ws.latn, w_k, w_uv, bl_c, num_heads, rows,
-                        stream);
-    if (st != MLA_OK) return st;
-    st = attention_common(output, q, dtype, ws.k_nope, ws.v_t, ws.krope, input_row_offsets,
-                          cache_lengths, bro_c, co_c, bl_c, batch_size, total_q, num_heads,
-                          rows, scale, attn_sink, ws.attn, stream);
-    if (st != MLA_OK) return st;
-  }
-  (void)fp8;
-  return MLA_OK;
+  return prefill_chunks(output, q, dtype, input_row_offsets, cache_lengths, kv_cache, dtype,
+                        false, page_table, buffer_row_offsets, cache_offsets, buffer_lengths,
+                        max_chunks, rows, w_k, w_uv, kv_norm_gamma, freqs_cis, batch_size,
+                        total_q, num_heads, page_size, max_pages_per_seq, num_pages,
+                        max_seq_len, scale, epsilon, attn_sink, workspace, stream);
 }
+
+static int decode_body(void* output, const void* q, const uint32_t* context_lengths,
+                       uint32_t add, const void* kv_cache, int32_t cache_dtype,
+                       const int32_t* page_table, const void* w_uk, const void* w_uv,
+                       int32_t batch_size, int32_t num_heads, int32_t page_size,
+                       int32_t max_pages_per_seq, int32_t num_pages, int32_t max_context_len,
+                       int32_t num_partitions, float scale, const float* attn_sink,
+                       void* workspace, hipStream_t stream);
 
 size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads, int32_t max_context_len,
                                  int32_t page_size, int32_t num_partitions, int32_t cache_dtype) {
@@ -459,6 +519,20 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                                                 page_size, num_partitions, cache_dtype);
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "mla_decode: workspace %zu < %zu", workspace_bytes, need);
+  return decode_body(output, q, context_lengths, 0, kv_cache, cache_dtype, page_table, w_uk,
+                     w_uv, batch_size, num_heads, page_size, max_pages_per_seq, num_pages,
+                     max_context_len, num_partitions, scale, attn_sink, workspace, stream);
+}
+
+// The absorbed decode (arguments already checked): context length of sequence
+// b is context_lengths[b] + add, at most max_context_len.
+static int decode_body(void* output, const void* q, const uint32_t* context_lengths,
+                       uint32_t add, const void* kv_cache, int32_t cache_dtype,
+                       const int32_t* page_table, const void* w_uk, const void* w_uv,
+                       int32_t batch_size, int32_t num_heads, int32_t page_size,
+                       int32_t max_pages_per_seq, int32_t num_pages, int32_t max_context_len,
+                       int32_t num_partitions, float scale, const float* attn_sink,
+                       void* workspace, hipStream_t stream) {
   DecodeWs ws = decode_ws_layout((char*)workspace, batch_size, num_heads, max_context_len,
                                  page_size, num_partitions, cache_dtype);
   const bool fp8 = cache_dtype == MLA_FP8_E4M3FN;
@@ -467,7 +541,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                                                 stream),
                       "absorb kernel");
   if (st != MLA_OK) return st;
-  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, batch_size,
+  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, add, batch_size,
                                             max_context_len, ws.wstart, ws.wspan, ws.wfirst,
                                             ws.G, stream),
                   "prefix kernel");
@@ -540,6 +614,123 @@ int mla_decode_sparse(void* output, const void* q, const int32_t* topk_lengths,
                     w_uk, w_uv, batch_size, num_heads, 1, indices_stride, num_rows,
                     max_topk, num_partitions, scale, attn_sink, workspace,
                     workspace_bytes, stream);
+}
+
+size_t mla_prefill_decode_workspace_size(int32_t batch_size, int32_t total_q,
+                                         int32_t num_heads, int32_t max_seq_len,
+                                         int32_t max_rows, int32_t max_cache_len,
+                                         int32_t page_size, int32_t indices_stride,
+                                         int32_t num_partitions, int32_t cache_dtype) {
+  if (batch_size < 1 || total_q < 0 || num_heads < 1 || max_seq_len < 0 || max_cache_len < 0 ||
+      page_size < 1 || indices_stride < 0 || num_partitions < 0 || !dtype_ok(cache_dtype))
+    return 0;
+  if (max_seq_len == 0) return kAlign;  // nothing runs; 0 stays the error value
+  if (max_seq_len > 1)
+    return mla_prefill_workspace_size(batch_size, total_q, num_heads, max_rows, MLA_BF16);
+  if (indices_stride > 0)
+    return mla_decode_sparse_workspace_size(batch_size, num_heads, indices_stride,
+                                            num_partitions, cache_dtype);
+  if (max_cache_len >= INT32_MAX) return 0;
+  return mla_decode_workspace_size(batch_size, num_heads, max_cache_len + 1, page_size,
+                                   num_partitions, cache_dtype);
+}
+
+int mla_prefill_decode(void* output, const void* q, const void* kv_input,
+                       const uint32_t* input_row_offsets, const uint32_t* cache_lengths,
+                       void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                       const uint32_t* buffer_row_offsets, const uint32_t* cache_offsets,
+                       const int32_t* buffer_lengths, int32_t max_chunks, int32_t max_rows,
+                       const void* w_k, const void* w_uk, const void* w_uv,
+                       const void* kv_norm_gamma, const void* freqs_cis, int32_t batch_size,
+                       int32_t total_q, int32_t num_heads, int32_t max_seq_len,
+                       int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                       int32_t max_cache_len, int32_t freqs_len, float scale, float epsilon,
+                       const int32_t* d_indices, int32_t indices_stride,
+                       const int32_t* topk_lengths, const float* attn_sink,
+                       int32_t num_partitions, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const char* who = "mla_prefill_decode";
+  // every check comes before the first launch
+  if (!input_row_offsets || !cache_lengths || !kv_cache || !page_table)
+    return fail(MLA_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "%s: cache dtype", who);
+  if (batch_size < 1 || total_q < 0 || num_heads < 1 || max_seq_len < 0 || page_size < 1 ||
+      max_pages_per_seq < 1 || num_pages < 1 || max_cache_len < 0 || freqs_len < 1 ||
+      num_partitions < 0 || num_partitions > 65536 || !(scale > 0.f) || !(epsilon >= 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "%s: sizes", who);
+  if ((max_seq_len == 0) != (total_q == 0))
+    return fail(MLA_ERR_INVALID_ARG, "%s: max_seq_len=%d with total_q=%d", who, max_seq_len,
+                total_q);
+  if ((uint64_t)num_pages * (uint64_t)page_size >= (1ull << 31))
+    return fail(MLA_ERR_INVALID_ARG, "%s: num_pages * page_size must be < 2^31", who);
+  if (kv_input) {
+    if (!kv_norm_gamma || !freqs_cis) return fail(MLA_ERR_INVALID_ARG, "%s: null pointer", who);
+    if (misaligned({kv_cache, kv_input, kv_norm_gamma, freqs_cis}))
+      return fail(MLA_ERR_INVALID_ARG, "%s: tensor not 16-byte aligned", who);
+  }
+  const bool sparse = d_indices != nullptr;
+  const int32_t num_rows = num_pages * page_size;
+  if (max_seq_len > 1) {
+    if (!output || !q || !buffer_row_offsets || !cache_offsets || !buffer_lengths || !w_k ||
+        !w_uv)
+      return fail(MLA_ERR_INVALID_ARG, "%s: null pointer (prefill)", who);
+    if (misaligned({output, q, kv_cache, w_k, w_uv, workspace}))
+      return fail(MLA_ERR_INVALID_ARG, "%s: tensor not 16-byte aligned", who);
+    if (num_heads > 1024 || max_chunks < 1 || max_rows < 1)
+      return fail(MLA_ERR_INVALID_ARG, "%s: sizes (prefill)", who);
+  } else if (max_seq_len == 1) {
+    if (!output || !q || !w_uk || !w_uv)
+      return fail(MLA_ERR_INVALID_ARG, "%s: null pointer (decode)", who);
+    if (misaligned({output, q, kv_cache, w_uk, w_uv, workspace}))
+      return fail(MLA_ERR_INVALID_ARG, "%s: tensor not 16-byte aligned", who);
+    if (num_heads > 128) return fail(MLA_ERR_INVALID_ARG, "%s: num_heads must be 1..128", who);
+    if (total_q != batch_size)
+      return fail(MLA_ERR_INVALID_ARG,
+                  "%s: decode takes one new token per sequence (total_q=%d, batch_size=%d)",
+                  who, total_q, batch_size);
+    if (sparse) {
+      if (!topk_lengths || indices_stride < 1)
+        return fail(MLA_ERR_INVALID_ARG, "%s: sparse decode needs topk_lengths and "
+                    "indices_stride >= 1", who);
+      if ((uint64_t)batch_size * (uint64_t)indices_stride >= (1ull << 31))
+        return fail(MLA_ERR_INVALID_ARG, "%s: batch_size * indices_stride must be < 2^31", who);
+    } else if ((uint64_t)batch_size * ((uint64_t)max_cache_len + 1) >= (1ull << 31)) {
+      return fail(MLA_ERR_INVALID_ARG, "%s: batch_size * (max_cache_len + 1) must be < 2^31",
+                  who);
+    }
+  }
+  const size_t need = mla_prefill_decode_workspace_size(
+      batch_size, total_q, num_heads, max_seq_len, max_rows, max_cache_len, page_size,
+      sparse ? indices_stride : 0, num_partitions, cache_dtype);
+  if (max_seq_len > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, workspace_bytes, need);
+
+  if (kv_input) {
+    const int st = kv_write_rows(kv_cache, cache_dtype, page_table, kv_input, input_row_offsets,
+                                 cache_lengths, kv_norm_gamma, freqs_cis, batch_size, total_q,
+                                 page_size, max_pages_per_seq, num_pages, freqs_len, epsilon,
+                                 stream);
+    if (st != MLA_OK) return st;
+  }
+  if (max_seq_len > 1) {
+    const int32_t rows = (max_rows + 63) / 64 * 64;
+    return prefill_chunks(output, q, MLA_BF16, input_row_offsets, cache_lengths, kv_cache,
+                          cache_dtype, true, page_table, buffer_row_offsets, cache_offsets,
+                          buffer_lengths, max_chunks, rows, w_k, w_uv, kv_norm_gamma, freqs_cis,
+                          batch_size, total_q, num_heads, page_size, max_pages_per_seq,
+                          num_pages, freqs_len, scale, epsilon, attn_sink, workspace, stream);
+  }
+  if (max_seq_len == 1) {
+    if (sparse)  // the listed rows as a paged context of one row per page
+      return decode_body(output, q, (const uint32_t*)topk_lengths, 0, kv_cache, cache_dtype,
+                         d_indices, w_uk, w_uv, batch_size, num_heads, 1, indices_stride,
+                         num_rows, indices_stride, num_partitions, scale, attn_sink, workspace,
+                         stream);
+    return decode_body(output, q, cache_lengths, 1, kv_cache, cache_dtype, page_table, w_uk,
+                       w_uv, batch_size, num_heads, page_size, max_pages_per_seq, num_pages,
+                       max_cache_len + 1, num_partitions, scale, attn_sink, workspace, stream);
+  }
+  return MLA_OK;
 }
 
 }  // extern "C"

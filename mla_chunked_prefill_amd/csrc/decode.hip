@@ -601,11 +601,13 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 // ---------------------------------------------------------------------------
 // prefix sums of the context lengths (one workgroup)
 // ---------------------------------------------------------------------------
-// Context lengths above max_ctx (the host's bound, which sized the ranges) are
-// taken as max_ctx, so the prefix sums stay below 2^31 whatever the device
-// holds; the results of such sequences are unspecified, their reads in bounds.
+// The context length of sequence b is ctx[b] + add (add is 1 when ctx holds
+// cache lengths that exclude the new token). Lengths above max_ctx (the
+// host's bound, which sized the ranges) are taken as max_ctx, so the prefix
+// sums stay below 2^31 whatever the device holds; the results of such
+// sequences are unspecified, their reads in bounds.
 __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const uint32_t* ctx,
-                                                            int B, uint32_t max_ctx,
+                                                            uint32_t add, int B, uint32_t max_ctx,
                                                             uint32_t* wstart, int2* wspan,
                                                             int32_t* wfirst, int G) {
   __shared__ uint32_t s_scan[256];
@@ -615,7 +617,7 @@ __global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const
   __syncthreads();
   for (int base = 0; base < B; base += 256) {
     const int b = base + tid;
-    const uint32_t v = b < B ? min(ctx[b], max_ctx) : 0u;
+    const uint32_t v = b < B ? (uint32_t)min((uint64_t)ctx[b] + add, (uint64_t)max_ctx) : 0u;
     s_scan[tid] = v;
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
@@ -799,10 +801,10 @@ hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16
   return hipGetLastError();
 }
 
-hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, int B, int max_ctx,
-                                uint32_t* wstart, int2* wspan, int32_t* wfirst, int G,
-                                hipStream_t stream) {
-  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, B,
+hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, uint32_t add, int B,
+                                int max_ctx, uint32_t* wstart, int2* wspan, int32_t* wfirst,
+                                int G, hipStream_t stream) {
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, add, B,
                      (uint32_t)max_ctx, wstart, wspan, wfirst, G);
   return hipGetLastError();
 }

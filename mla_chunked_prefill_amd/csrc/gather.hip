@@ -26,7 +26,27 @@ __device__ __forceinline__ int find_seq(const uint32_t* __restrict__ bro, int B,
   return lo;
 }
 
-template <bool kFp8Cache, bool kFp8Rope>
+// 8 rope values of a buffer row, lanes 0-7: e4m3 (saturating) or bf16
+template <bool kFp8Rope>
+__device__ __forceinline__ void store_rope(void* krope, int row, int lane, const float* r) {
+  if (kFp8Rope) {
+    u32x2 w;
+    w[0] = f32_to_e4m3_sat(r[0]) | (f32_to_e4m3_sat(r[1]) << 8) |
+           (f32_to_e4m3_sat(r[2]) << 16) | (f32_to_e4m3_sat(r[3]) << 24);
+    w[1] = f32_to_e4m3_sat(r[4]) | (f32_to_e4m3_sat(r[5]) << 8) |
+           (f32_to_e4m3_sat(r[6]) << 16) | (f32_to_e4m3_sat(r[7]) << 24);
+    *(u32x2*)((uint8_t*)krope + (size_t)row * kRope + lane * 8) = w;
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(r[2 * i], r[2 * i + 1]);
+    *(u32x4*)((uint16_t*)krope + (size_t)row * kRope + lane * 8) = w;
+  }
+}
+
+// kProcessed: the pool holds rows already normalised and rotated (as the KV
+// write path stores them); they are copied into the buffers unchanged.
+template <bool kFp8Cache, bool kFp8Rope, bool kProcessed>
 __global__ void __launch_bounds__(64 * kGatherRowsPerBlock)
 gather_norm_rope_kernel(GatherArgs a) {
   const int nrows = *a.bl_c;
@@ -38,7 +58,7 @@ gather_norm_rope_kernel(GatherArgs a) {
   const uint32_t lp = p / (uint32_t)a.ps;
   int page = -1;
   if (lp < (uint32_t)a.maxp) page = a.page_table[(size_t)b * a.maxp + lp];
-  const bool ok = page >= 0 && page < a.num_pages && p < (uint32_t)a.max_seq_len;
+  const bool ok = page >= 0 && page < a.num_pages && (kProcessed || p < (uint32_t)a.max_seq_len);
   const size_t slot = ok ? (size_t)page * a.ps + (p % (uint32_t)a.ps) : 0;
 
   float x[8];
@@ -77,6 +97,15 @@ gather_norm_rope_kernel(GatherArgs a) {
     }
   }
 
+  if (kProcessed) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    *(u32x4*)(a.latn + (size_t)row * kLora + lane * 8) = o;
+    if (lane < 8) store_rope<kFp8Rope>(a.krope, row, lane, y);
+    return;
+  }
+
   // RMSNorm of the latent
   float ss = 0.f;
 #pragma unroll
@@ -105,19 +134,7 @@ gather_norm_rope_kernel(GatherArgs a) {
       r[2 * i] = y[2 * i] * c - y[2 * i + 1] * s;
       r[2 * i + 1] = y[2 * i] * s + y[2 * i + 1] * c;
     }
-    if (kFp8Rope) {
-      u32x2 w;
-      w[0] = f32_to_e4m3_sat(r[0]) | (f32_to_e4m3_sat(r[1]) << 8) |
-             (f32_to_e4m3_sat(r[2]) << 16) | (f32_to_e4m3_sat(r[3]) << 24);
-      w[1] = f32_to_e4m3_sat(r[4]) | (f32_to_e4m3_sat(r[5]) << 8) |
-             (f32_to_e4m3_sat(r[6]) << 16) | (f32_to_e4m3_sat(r[7]) << 24);
-      *(u32x2*)((uint8_t*)a.krope + (size_t)row * kRope + lane * 8) = w;
-    } else {
-      u32x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(r[2 * i], r[2 * i + 1]);
-      *(u32x4*)((uint16_t*)a.krope + (size_t)row * kRope + lane * 8) = w;
-    }
+    store_rope<kFp8Rope>(a.krope, row, lane, r);
   }
 }
 
@@ -207,17 +224,24 @@ hipError_t launch_kv_write(const KvWriteArgs& a, bool fp8_cache, hipStream_t str
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& a, bool fp8_cache, bool fp8_rope,
+template <bool kProcessed>
+void launch_gather_t(const GatherArgs& a, bool fp8_cache, bool fp8_rope, dim3 grid, dim3 block,
+                     hipStream_t stream) {
+  if (fp8_cache) {
+    if (fp8_rope) hipLaunchKernelGGL((gather_norm_rope_kernel<true, true, kProcessed>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gather_norm_rope_kernel<true, false, kProcessed>), grid, block, 0, stream, a);
+  } else {
+    if (fp8_rope) hipLaunchKernelGGL((gather_norm_rope_kernel<false, true, kProcessed>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gather_norm_rope_kernel<false, false, kProcessed>), grid, block, 0, stream, a);
+  }
+}
+
+hipError_t launch_gather(const GatherArgs& a, bool fp8_cache, bool fp8_rope, bool processed,
                          hipStream_t stream) {
   const dim3 grid((a.max_rows + kGatherRowsPerBlock - 1) / kGatherRowsPerBlock);
   const dim3 block(64 * kGatherRowsPerBlock);
-  if (fp8_cache) {
-    if (fp8_rope) hipLaunchKernelGGL((gather_norm_rope_kernel<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gather_norm_rope_kernel<true, false>), grid, block, 0, stream, a);
-  } else {
-    if (fp8_rope) hipLaunchKernelGGL((gather_norm_rope_kernel<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gather_norm_rope_kernel<false, false>), grid, block, 0, stream, a);
-  }
+  if (processed) launch_gather_t<true>(a, fp8_cache, fp8_rope, grid, block, stream);
+  else launch_gather_t<false>(a, fp8_cache, fp8_rope, grid, block, stream);
   return hipGetLastError();
 }
 

@@ -88,7 +88,8 @@ struct CombineArgs {
 };
 hipError_t launch_plan(uint32_t*, uint32_t*, int32_t*, uint32_t*, const uint32_t*,
                        const uint32_t*, int, int, uint32_t, hipStream_t);
-hipError_t launch_gather(const GatherArgs&, bool, bool, hipStream_t);
+// fp8 cache, fp8 krope, processed (rows copied as stored, no RMSNorm/RoPE)
+hipError_t launch_gather(const GatherArgs&, bool, bool, bool, hipStream_t);
 hipError_t launch_kv_write(const KvWriteArgs&, bool, hipStream_t);
 hipError_t launch_up_project(const GemmArgs&, bool, hipStream_t);
 int attn_num_slots(int B, int total_q);
@@ -97,8 +98,10 @@ hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
 hipError_t launch_decode_absorb(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                 hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
-hipError_t launch_decode_prefix(uint32_t*, const uint32_t*, int, int, uint32_t*, int2*,
-                                int32_t*, int, hipStream_t);
+// context length of sequence b: min(ctx[b] + add, max_ctx)
+hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, uint32_t add, int B,
+                                int max_ctx, uint32_t* wstart, int2* wspan, int32_t* wfirst,
+                                int G, hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);

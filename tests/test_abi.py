@@ -92,3 +92,45 @@ def test_workspace_sizes_grow_with_problem(lib):
     assert 0 < a < b and c < b
     assert lib.mla_prefill_workspace_size(0, 100, 4, 512, 0) == 0
     assert lib.mla_prefill_attention_workspace_size(2, 100, 4) < a
+
+
+def _unified_call(lib, **over):
+    """mla_prefill_decode with fake device pointers (never dereferenced: every
+    case below fails, or has nothing to do, before the first launch)."""
+    fake = ctypes.c_void_p(0x1000)
+    a = dict(output=fake, q=fake, kv_input=None, offs=fake, clen=fake, cache=fake, cache_dtype=0,
+             page_table=fake, bro=fake, co=fake, bl=fake, max_chunks=2, max_rows=512, w_k=fake,
+             w_uk=fake, w_uv=fake, gamma=fake, freqs=fake, B=4, total_q=4, H=8, max_seq_len=1,
+             ps=16, maxp=64, num_pages=100, max_cache_len=900, freqs_len=1024, scale=0.1,
+             eps=1e-6, d_indices=None, stride=0, topk=None, sink=None, num_partitions=0,
+             ws=fake, ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return lib.mla_prefill_decode(*a.values())
+
+
+def test_unified_entry_checks_and_workspace(lib):
+    fake = ctypes.c_void_p(0x1000)
+    # decode takes one token per sequence
+    assert _unified_call(lib, total_q=5) == -1
+    assert b"one new token" in lib.mla_last_error()
+    # max_seq_len 0 goes with total_q 0; then there is nothing to do
+    assert _unified_call(lib, max_seq_len=0) == -1
+    assert _unified_call(lib, max_seq_len=0, total_q=0, ws=None, ws_bytes=0) == 0
+    # prefill needs the plan and w_k
+    assert _unified_call(lib, max_seq_len=7, total_q=20, bro=None) == -1
+    assert _unified_call(lib, max_seq_len=7, total_q=20, w_k=None) == -1
+    # sparse decode needs the lengths and a positive stride
+    assert _unified_call(lib, d_indices=fake, stride=64) == -1
+    assert _unified_call(lib, d_indices=fake, topk=fake, stride=0) == -1
+    # a KV write needs gamma and freqs
+    assert _unified_call(lib, kv_input=fake, gamma=None) == -1
+    # workspaces: the selected branch's, and too small is rejected
+    dec = lib.mla_prefill_decode_workspace_size(4, 4, 8, 1, 0, 900, 16, 0, 0, 0)
+    assert dec == lib.mla_decode_workspace_size(4, 8, 901, 16, 0, 0) > 0
+    sp = lib.mla_prefill_decode_workspace_size(4, 4, 8, 1, 0, 900, 16, 64, 0, 1)
+    assert sp == lib.mla_decode_sparse_workspace_size(4, 8, 64, 0, 1) > 0
+    pf = lib.mla_prefill_decode_workspace_size(4, 20, 8, 7, 512, 900, 16, 0, 0, 0)
+    assert pf == lib.mla_prefill_workspace_size(4, 20, 8, 512, 0) > 0
+    assert lib.mla_prefill_decode_workspace_size(0, 4, 8, 1, 0, 900, 16, 0, 0, 0) == 0
+    assert _unified_call(lib, ws_bytes=dec - 1) == -3
+    assert _unified_call(lib, max_seq_len=7, total_q=20, ws_bytes=pf - 1) == -3

@@ -608,3 +608,195 @@ def test_decode_sparse_sinks(B):
     ref = oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
                                dec.nope, dec.lora, sinks=np.array(sinks))
     _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
+
+
+# ---------------------------------------------------------------------------
+# the graph op as one call: KV write, then prefill or decode by max_seq_len
+# ---------------------------------------------------------------------------
+
+def _round_to_storage(vals, fp8):
+    v = np.asarray(vals, dtype=np.float32)
+    return f32_to_e4m3fn_codes(v) if fp8 else f32_to_bf16_bits(v)
+
+
+def _decoded(bits, fp8):
+    return oracle.e4m3fn_to_f64(bits) if fp8 else oracle.bf16_to_f64(bits)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_unified_prefill_writes_then_attends_over_stored_rows(B, fp8):
+    # several chunks of 256 tokens, ragged prompts, an empty one, pages of 16;
+    # the pool's cached rows are taken as stored rows, the new tokens come in raw
+    wl = make_prefill("uni", 91, [300, 77, 0, 129, 1], [0, 250, 33, 1000, 5], 4, 16, 256)
+    pool = _round_to_storage(oracle.bf16_to_f64(wl.pool), fp8)
+    rng = np.random.default_rng(92)
+    x, gamma = _kv_raw(rng, wl.total_q)
+    t = prefill_tensors(wl)
+    cache = _dev_pool(pool, fp8)
+    _say(f"unified prefill fp8_cache={fp8}")
+    out = B.prefill_decode(t["q"], t["input_row_offsets"], t["cache_lengths"], cache,
+                           t["page_table"], t["w_uk"], t["w_uv"], _dev_bf16(gamma),
+                           t["freqs_cis"], int(wl.new_lens.max()), int(wl.cached_lens.max()),
+                           wl.scale, wl.eps, kv_input=_dev_bf16(x), w_k=t["w_k"],
+                           buffer_token_size=wl.buffer_token_size, max_chunks=wl.max_chunks)
+    torch.cuda.synchronize()
+    dec = oracle.Decoded(wl)
+    written = oracle.kv_write(_decoded(pool, fp8), wl.page_table, oracle.bf16_to_f64(x),
+                              wl.input_row_offsets, wl.cache_lengths, oracle.bf16_to_f64(gamma),
+                              dec.freqs, wl.eps, wl.page_size)
+    stored = _decoded(_round_to_storage(written, fp8), fp8)
+    ref, _ = oracle.prefill_decode(dec.q, dec.offs, dec.clen, stored, wl.page_table,
+                                   wl.page_size, dec.w_k, dec.w_uk, dec.w_uv, dec.gamma,
+                                   dec.freqs, wl.scale, wl.eps, int(wl.new_lens.max()))
+    _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
+    got_pool = _decoded(fp8_bits(cache) if fp8 else bf16_bits(cache), fp8)
+    assert (np.abs(got_pool - written) <= _stored_bound(written, fp8)).all()
+
+
+@pytest.mark.parametrize("fp8,parts", [(False, 0), (False, 5), (True, 0)])
+def test_unified_decode_writes_the_token_then_attends(B, fp8, parts):
+    wl = make_decode("udec", 93, [300, 1, 1000, 77, 2500], 16, 16, fp8=fp8)
+    ctx = wl.context_lens.astype(np.int64)
+    rng = np.random.default_rng(94)
+    x, gamma = _kv_raw(rng, len(ctx))
+    freqs = rope_table_bits(int(ctx.max()), 64)
+    off = np.arange(len(ctx) + 1, dtype=np.uint32)
+    t = decode_tensors(wl)
+    _say(f"unified decode fp8_cache={fp8} parts={parts}")
+    out = B.prefill_decode(t["q"], _u32(off), _u32(ctx - 1), t["kv_cache"], t["page_table"],
+                           t["w_uk"], t["w_uv"], _dev_bf16(gamma), _dev_bf16(freqs), 1,
+                           int(ctx.max()) - 1, wl.scale, 1e-6, kv_input=_dev_bf16(x),
+                           num_partitions=parts)
+    # the dense decode entry over the same written pool runs the same kernels
+    same = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
+                    t["w_uv"], int(ctx.max()), wl.scale, num_partitions=parts)
+    torch.cuda.synchronize()
+    assert torch.equal(out, same)
+    vals = oracle.kv_write(_decoded(wl.pool, fp8), wl.page_table, oracle.bf16_to_f64(x), off,
+                           ctx - 1, oracle.bf16_to_f64(gamma), oracle.bf16_to_f64(freqs), 1e-6,
+                           wl.page_size)
+    ref = oracle.decode(dataclasses.replace(wl, pool=_round_to_storage(vals, fp8)))
+    _assert_close(_f64(out), ref, FP8_MAX if fp8 else BF16_MAX, None if fp8 else BF16_MEAN)
+
+
+def test_unified_sparse_decode_with_sinks(B):
+    wl = make_decode("usp", 95, [2000, 900, 3000], 16, 16)
+    lens = [5, 300, 0]
+    idx = _sparse_case(wl, lens, 96)
+    sinks = [1.0, -2.0, 3.0]
+    ctx = wl.context_lens.astype(np.int64)
+    t = decode_tensors(wl)
+    gamma = _dev_bf16(f32_to_bf16_bits(np.ones(512, np.float32)))
+    freqs = _dev_bf16(rope_table_bits(int(ctx.max()), 64))
+    out = B.prefill_decode(t["q"], _u32(np.arange(len(ctx) + 1)), _u32(ctx - 1), t["kv_cache"],
+                           t["page_table"], t["w_uk"], t["w_uv"], gamma, freqs, 1,
+                           int(ctx.max()) - 1, wl.scale, 1e-6,
+                           d_indices=torch.from_numpy(idx).cuda(),
+                           topk_lengths=torch.from_numpy(np.asarray(lens, np.int32)).cuda(),
+                           attn_sink=_sinks(sinks))
+    torch.cuda.synchronize()
+    dec = oracle.DecodedDecode(wl)
+    ref = oracle.decode_sparse(dec.q, dec.pool, idx, lens, dec.w_uk, dec.w_uv, wl.scale,
+                               dec.nope, dec.lora, sinks=np.array(sinks))
+    _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
+
+
+def test_unified_calls_replay_from_a_captured_graph(B):
+    # every grid and the partition count are host values: a captured call
+    # replays with new device data (queries, cache lengths) and matches the
+    # eager call on the same data bit for bit
+    wl = make_decode("ugr", 97, [700, 1, 2000, 64], 8, 16)
+    ctx = wl.context_lens.astype(np.int64)
+    t = decode_tensors(wl)
+    Bn, H = wl.batch, wl.num_heads
+    off = _u32(np.arange(Bn + 1))
+    clen = _u32(ctx - 1)
+    gamma = _dev_bf16(f32_to_bf16_bits(np.ones(512, np.float32)))
+    freqs = _dev_bf16(rope_table_bits(int(ctx.max()), 64))
+    max_cache = int(ctx.max()) - 1
+    parts = 7
+    nbytes = B.mla_prefill_decode_workspace_size(Bn, Bn, H, 1, 0, max_cache, wl.page_size, 0,
+                                                 parts, B.MLA_BF16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((Bn, H, 128), dtype=torch.bfloat16, device="cuda")
+    ref_out = torch.empty_like(out)
+
+    def call(o, w):
+        B.mla_prefill_decode(o, t["q"], off, clen, t["kv_cache"], t["page_table"], t["w_uk"],
+                             t["w_uv"], gamma, freqs, 1, max_cache, wl.scale, 1e-6, w,
+                             num_partitions=parts)
+
+    call(out, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, ws)
+    rng = np.random.default_rng(98)
+    for rep in range(3):
+        qn = f32_to_bf16_bits(rng.standard_normal(wl.q.shape).astype(np.float32))
+        t["q"].copy_(_dev_bf16(qn))
+        new_ctx = np.maximum(1, ctx - rng.integers(0, 50, size=Bn))
+        clen.copy_(_u32(new_ctx - 1))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        call(ref_out, ws2)
+        torch.cuda.synchronize()
+        _say(f"graph replay {rep}")
+        assert torch.equal(got, ref_out)
+        if rep == 0:
+            ref = oracle.decode(dataclasses.replace(wl, q=qn,
+                                                    context_lens=new_ctx.astype(np.uint32)))
+            _assert_close(_f64(got), ref, BF16_MAX, BF16_MEAN)
+
+
+def test_unified_prefill_with_its_plan_replays_from_a_captured_graph(B):
+    wl = make_prefill("ugp", 99, [130, 0, 64], [40, 7, 200], 2, 16, 128)
+    t = prefill_tensors(wl)
+    Bn, H, Tq = wl.batch, wl.num_heads, wl.total_q
+    C, T = wl.max_chunks, wl.buffer_token_size
+    bro = torch.empty((C, Bn + 1), dtype=torch.uint32, device="cuda")
+    co = torch.empty((C, Bn), dtype=torch.uint32, device="cuda")
+    bl = torch.empty((C,), dtype=torch.int32, device="cuda")
+    max_rows = Bn * T
+    nbytes = B.mla_prefill_decode_workspace_size(Bn, Tq, H, int(wl.new_lens.max()), max_rows,
+                                                 int(wl.cached_lens.max()), wl.page_size, 0, 0,
+                                                 B.MLA_BF16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((Tq, H, 128), dtype=torch.bfloat16, device="cuda")
+
+    def call(o):
+        B.mla_prefill_plan(bro, co, bl, t["input_row_offsets"], t["cache_lengths"], T)
+        B.mla_prefill_decode(o, t["q"], t["input_row_offsets"], t["cache_lengths"],
+                             t["kv_cache"], t["page_table"], t["w_uk"], t["w_uv"],
+                             t["kv_norm_gamma"], t["freqs_cis"], int(wl.new_lens.max()),
+                             int(wl.cached_lens.max()), wl.scale, wl.eps, ws, w_k=t["w_k"],
+                             plan_tensors=(bro, co, bl), max_rows=max_rows)
+
+    call(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    rng = np.random.default_rng(100)
+    ref_out = torch.empty_like(out)
+    for rep in range(3):
+        qn = f32_to_bf16_bits(rng.standard_normal(wl.q.shape).astype(np.float32))
+        t["q"].copy_(_dev_bf16(qn))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        call(ref_out)
+        torch.cuda.synchronize()
+        _say(f"prefill graph replay {rep}")
+        assert torch.equal(got, ref_out)
+        if rep == 0:
+            dec = oracle.Decoded(dataclasses.replace(wl, q=qn))
+            ref, _ = oracle.prefill_decode(dec.q, dec.offs, dec.clen, dec.pool, wl.page_table,
+                                           wl.page_size, dec.w_k, dec.w_uk, dec.w_uv,
+                                           dec.gamma, dec.freqs, wl.scale, wl.eps,
+                                           int(wl.new_lens.max()))
+            _assert_close(_f64(got), ref, BF16_MAX, BF16_MEAN)
