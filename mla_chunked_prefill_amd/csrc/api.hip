@@ -536,15 +536,20 @@ static int decode_body(void* output, const void* q, const uint32_t* context_leng
   DecodeWs ws = decode_ws_layout((char*)workspace, batch_size, num_heads, max_context_len,
                                  page_size, num_partitions, cache_dtype);
   const bool fp8 = cache_dtype == MLA_FP8_E4M3FN;
+  mla::PrefixArgs pa;
+  pa.cum = ws.cum;
+  pa.ctx = context_lengths;
+  pa.add = add;
+  pa.B = batch_size;
+  pa.max_ctx = (uint32_t)max_context_len;
+  pa.wstart = ws.wstart;
+  pa.wspan = ws.wspan;
+  pa.wfirst = ws.wfirst;
+  pa.G = ws.G;
   int st = hip_status(mla::launch_decode_absorb(ws.q_abs, (const uint16_t*)q,
-                                                (const uint16_t*)w_uk, batch_size, num_heads,
+                                                (const uint16_t*)w_uk, batch_size, num_heads, pa,
                                                 stream),
                       "absorb kernel");
-  if (st != MLA_OK) return st;
-  st = hip_status(mla::launch_decode_prefix(ws.cum, context_lengths, add, batch_size,
-                                            max_context_len, ws.wstart, ws.wspan, ws.wfirst,
-                                            ws.G, stream),
-                  "prefix kernel");
   if (st != MLA_OK) return st;
   mla::DecodeArgs a;
   a.q_abs = (const uint16_t*)ws.q_abs;

@@ -12,8 +12,8 @@
 //               softmax state (max, sum, O_lat) per sequence it touches.
 //  3. combine:  per (sequence, head), the states of the key ranges that
 //               touched the sequence are merged by log-sum-exp into o_lat.
-//  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA, the 512-long
-//               reduction split over the waves of a workgroup.
+//  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA, one wave per
+//               32 x 32 output tile.
 #include "kernels.hpp"
 
 namespace mla {
@@ -27,14 +27,97 @@ namespace mla {
 // the reduction), then runs its MFMAs. A lane's 16-byte operand fragment is
 // row l32 of a 32-row block, reduction elements 16 k + 8 hf .. + 7.
 
+// ---------------------------------------------------------------------------
+// prefix sums of the context lengths (one workgroup)
+// ---------------------------------------------------------------------------
+// The context length of sequence b is ctx[b] + add (add is 1 when ctx holds
+// cache lengths that exclude the new token). Lengths above max_ctx (the
+// host's bound, which sized the ranges) are taken as max_ctx, so the prefix
+// sums stay below 2^31 whatever the device holds; the results of such
+// sequences are unspecified, their reads in bounds.
+// Run by one workgroup of 256 threads (the extra column of the absorb grid).
+__device__ void decode_prefix(const PrefixArgs& pa) {
+  uint32_t* cum = pa.cum;
+  const uint32_t* ctx = pa.ctx;
+  const uint32_t add = pa.add;
+  const int B = pa.B;
+  const uint32_t max_ctx = pa.max_ctx;
+  uint32_t* wstart = pa.wstart;
+  int2* wspan = pa.wspan;
+  int32_t* wfirst = pa.wfirst;
+  const int G = pa.G;
+  __shared__ uint32_t s_scan[256];
+  __shared__ uint32_t s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    const uint32_t v = b < B ? (uint32_t)min((uint64_t)ctx[b] + add, (uint64_t)max_ctx) : 0u;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const uint32_t x = tid >= d ? s_scan[tid - d] : 0u;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    if (b < B) cum[b + 1] = s_carry + s_scan[tid];
+    __syncthreads();
+    if (tid == 255) s_carry += s_scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) cum[0] = 0;
+  // key range w covers keys [wstart[w], wstart[w+1])
+  const uint32_t N = s_carry;
+  for (int w = tid; w <= G; w += 256) wstart[w] = (uint32_t)(((uint64_t)w * N) / G);
+  __threadfence();  // other threads of the workgroup read these entries below
+  __syncthreads();
+  // first sequence of every key range: largest b with cum[b] <= wstart[w]
+  for (int w = tid; w < G; w += 256) {
+    const uint32_t key = wstart[w];
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    wfirst[w] = lo;
+  }
+  // ranges holding sequence b's first and last keys (empty sequences: (0, -1))
+  for (int b = tid; b < B; b += 256) {
+    const uint32_t lo_key = cum[b], hi_key = cum[b + 1];
+    if (hi_key <= lo_key) { wspan[b] = make_int2(0, -1); continue; }
+    int lo = 0, hi = G - 1;  // largest w with wstart[w] <= lo_key
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wstart[mid] <= lo_key) lo = mid; else hi = mid - 1;
+    }
+    const int w_lo = lo;
+    hi = G - 1;              // largest w with wstart[w] < hi_key
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wstart[mid] < hi_key) lo = mid; else hi = mid - 1;
+    }
+    wspan[b] = make_int2(w_lo, lo);
+  }
+}
+
 // q_abs[b, h, 0:512] = w_uk[h] q_nope[b, h]; q_abs[b, h, 512:576] = q_rope[b, h].
-// Grid (512 / 128, H, ceil(B / 64)); wave v computes latent dims
-// 128 blockIdx.x + 32 v .. + 31 for 64 sequences (two 32-row blocks). The
-// workgroups of column block 0 also copy the rope part of their sequences.
+// Grid (512 / 128 + 1, H, ceil(B / 64)); wave v of column block x < 4 computes
+// latent dims 128 x + 32 v .. + 31 for 64 sequences (two 32-sequence blocks)
+// as D = W Q^T, so that a lane holds four runs of four consecutive dims of
+// one sequence; an exchange with the lane 32 away turns them into two runs
+// of eight, each stored with one 16-byte store. The workgroups of column
+// block 0 also copy the rope part of their sequences; workgroup (4, 0, 0)
+// computes the split-KV prefix sums, the rest of column 4 exits.
 __global__ void __launch_bounds__(256) absorb_kernel(uint16_t* __restrict__ q_abs,
                                                      const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ w_uk, int B,
-                                                     int H) {
+                                                     int H, PrefixArgs pa) {
+  if (blockIdx.x == kLora / 128) {
+    if (blockIdx.y == 0 && blockIdx.z == 0) decode_prefix(pa);
+    return;
+  }
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int h = blockIdx.y;
@@ -55,25 +138,41 @@ __global__ void __launch_bounds__(256) absorb_kernel(uint16_t* __restrict__ q_ab
       if (brow >= B) xf[bt][k] = u32x4{0, 0, 0, 0};
     }
   }
-  f32x16 acc[2];
 #pragma unroll
   for (int bt = 0; bt < 2; ++bt) {
+    f32x16 acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[bt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int k = 0; k < kSteps; ++k)
-      acc[bt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xf[bt][k]),
-                                                        __builtin_bit_cast(bf16x8, wf[k]), acc[bt],
-                                                        0, 0, 0);
-  }
-  // lane holds latent dim n0 + l32 of rows b0 + 32 bt + 8 (i / 4) + 4 hf + i % 4
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[k]),
+                                                    __builtin_bit_cast(bf16x8, xf[bt][k]), acc,
+                                                    0, 0, 0);
+    // lane holds sequence b0 + 32 bt + l32, dims n0 + 8 (i / 4) + 4 hf + i % 4
+    const int b = b0 + 32 * bt + l32;
 #pragma unroll
-  for (int bt = 0; bt < 2; ++bt)
+    for (int pr = 0; pr < 2; ++pr) {
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int b = b0 + 32 * bt + (i >> 2) * 8 + hf * 4 + (i & 3);
-      if (b < B) q_abs[((size_t)b * H + h) * kCache + n0 + l32] = (uint16_t)f32_to_bf16_rne(acc[bt][i]);
+      for (int e = 0; e < 4; e += 2) {
+        uint32_t x[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // lanes 0-31 keep odd-group values and take the upper lanes' ones;
+          // lanes 32-63 take the lower lanes' even-group values
+          const auto r = __builtin_amdgcn_permlane32_swap(
+              __float_as_uint(acc[(2 * pr + 1) * 4 + e + u]),
+              __float_as_uint(acc[(2 * pr) * 4 + e + u]), false, false);
+          x[u][0] = r[0];
+          x[u][1] = r[1];
+        }
+        o[e / 2] = pack_bf16x2(__uint_as_float(x[0][0]), __uint_as_float(x[1][0]));
+        o[2 + e / 2] = pack_bf16x2(__uint_as_float(x[0][1]), __uint_as_float(x[1][1]));
+      }
+      const int dim0 = n0 + 8 * (2 * pr + (hf ^ 1));
+      if (b < B) *(u32x4*)(q_abs + ((size_t)b * H + h) * kCache + dim0) = o;
     }
+  }
   if (blockIdx.x == 0) {
     // 64 sequences x 64 rope values: 512 pieces of 16 bytes
 #pragma unroll
@@ -171,9 +270,13 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
 // against their exact maximum.
 //
 // Tiles are aligned to 32 keys of the sequence (keys of the first tile before
-// the range start are masked). Four LDS stages hold tiles t .. t+3: the loads
-// of tile t+3 go out while tile t is computed, three tiles ahead of use, one
-// barrier per tile. When the page size is a multiple of 32 a tile is 32
+// the range start are masked), one barrier per tile, four LDS stages. bf16:
+// a wave computes tile t's scores, then tile t-1's value product with tile
+// t's softmax placed between its MFMAs (those MFMAs wait on LDS reads, which
+// leaves room for the vector work); the stages hold tiles t-1 .. t+2 and the
+// loads of tile t+2 go out while tile t's scores are computed. e4m3: each
+// tile's scores, softmax and value product in turn, the stages holding tiles
+// t .. t+3, loads three tiles ahead. When the page size is a multiple of 32 a tile is 32
 // consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its direct
 // loads are spread between the score MFMAs; otherwise every row's pool slot
 // is looked up and the loads go out in one burst. A bf16 row keeps its 72
@@ -418,143 +521,48 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     float l_run = 0.f;
     bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
-    for (int t = 0; t < min(3, ntiles); ++t) issue(t);
-    // e4m3: each wave waits for its own loads of tile tt and widens exactly
-    // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
-    // one row) into bf16 stage tt % 2; the barrier at the top of the tile
-    // loop then publishes the whole tile. later: tiles issued after tt whose
-    // loads may stay in flight.
-    auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
-      if (later == 2) {
-        if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      } else if (later == 1) {
-        if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      const uint8_t* F = sZ + kStage0 + (tt % 4) * kF8StageB;
-      uint8_t* D = sZ + (tt % 2) * kZStageB;
+    if constexpr (!kFp8) {
+      // bf16: tile t's scores, then tile t-1's value product with tile t's
+      // softmax interleaved between its MFMAs (the value MFMAs wait on LDS
+      // reads; the softmax fills those gaps). Stages hold tiles t-1 (value
+      // product), t (scores), t+1 and t+2 (loads in flight): the loads of
+      // tile t+2 go out once the barrier of tile t shows every wave done
+      // with tile t-2.
+      for (int t = 0; t < min(2, ntiles); ++t) issue(t);
+      auto scores_t = [&](const uint8_t* Zs, const void* sbn, uint32_t nbase, auto with_dma)
+          __attribute__((always_inline)) {
+        f32x16 acc;
 #pragma unroll
-      for (int j = 0; j < kF8LoadsPerWave; ++j) {
-        const int p = wave + kDecWaves * j;
-        if (p < kF8Loads) {
-          const int byte = p * 1024 + lane * 16;
-          const int r = byte / kF8RowB;
-          const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
-          const u32x4 v = *(const u32x4*)(F + byte);
-          *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
-          *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
-        }
-      }
-    };
-    if constexpr (kFp8) widen_own(0, min(2, ntiles - 1));
-
-    for (int t = 0; t < ntiles; ++t) {
-      // wait for this wave's loads of tile t; those of the (at most two) later
-      // tiles already issued may stay in flight
-      if constexpr (!kFp8) {
-        const int later = min(2, ntiles - 1 - t);
-        if (later == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
-      // tile t is in place for every wave (bf16: landed; e4m3: widened); every
-      // wave is done with tile t-1, whose stage receives tile t+3 (e4m3: its
-      // bf16 stage receives tile t+1 at the end of this iteration)
-      __syncthreads();
-      // bf16: tile t+3's loads are spread between the score MFMAs below when
-      // it comes in one piece; e4m3 (five loads a wave) issues them at once
-      const bool spread = !kFp8 && t + 3 < ntiles && one_piece(t + 3);
-      const void* sbn = cache;
-      if (spread) {
-        sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 3) * kDecBN) *
-                                        (kFp8 ? kF8RowB : kZRowB));
-      } else if (t + 3 < ntiles) {
-        issue(t + 3);
-      }
-      const uint32_t nbase = lds0 + kStage0 + ((t + 3) % 4) * kStageB;
-      const uint8_t* Z = sZ + (kFp8 ? (t % 2) : (t % 4)) * kZStageB;
-      const int kt = kt0 + t * kDecBN;
-
-      // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
-      auto scores = [&](auto with_dma) __attribute__((always_inline)) {
-        f32x16 sa, sb;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { sa[i] = 0.f; sb[i] = 0.f; }
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
         constexpr int kAhead = 4;
-        constexpr int kEvery = kFp8 ? 8 : 4;  // one load per 4 (e4m3: 8) score steps
         bf16x8 zb[kAhead];
         auto zload = [&](int ks) __attribute__((always_inline)) {
-          return *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
+          return *(const bf16x8*)(Zs + s_base[ks & 3] + 128 * (ks >> 2));
         };
 #pragma unroll
         for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
 #pragma unroll
         for (int ks = 0; ks < kQSteps; ++ks) {
-          if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sb, 0, 0, 0);
-          else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sa, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], acc, 0, 0, 0);
           if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
           if constexpr (decltype(with_dma)::value) {
-            if (ks % kEvery == 0 && ks / kEvery < kLoadsPerWave) {
-              const int j = ks / kEvery;
-              if (!kFp8 || j < kLoadsPerWave - 1 || wave + kDecWaves * j < kF8Loads)
-                dma16_s_nb(sbn, dma_off(j), nbase + (wave + kDecWaves * j) * 1024);
-            }
+            if (ks % 4 == 0 && ks / 4 < kZLoadsPerWave)
+              dma16_s_nb(sbn, dma_off(ks / 4), nbase + (wave + kDecWaves * (ks / 4)) * 1024);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sa[i] += sb[i];
-        return sa;
+        return acc;
       };
-      f32x16 s = spread ? scores(std::integral_constant<bool, true>())
-                        : scores(std::integral_constant<bool, false>());
-
-      // register i holds tile row 16*(i/8) + 8*hf + i%8
-      if (kt < k0 || kt + kDecBN > k1) {
-        const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int c = (i >> 3) * 16 + (i & 7);
-          if (c < lo || c >= hi) s[i] = -INFINITY;
-        }
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-      const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
-      m_seen = fmaxf(m_seen, mt);
-      if (t == 0) m_ref = mt;
-      halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
-      const float neg_m = -m_ref;
-      float psum = 0.f;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 wv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j], sl2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j + 1], sl2, neg_m));
-          psum += p0 + p1;
-          wv[j] = pack_bf16x2(p0, p1);
-        }
-        pb[ks] = __builtin_bit_cast(bf16x8, wv);
-      }
-      l_run += sum_with_lane32(psum);
-
-      // ---- O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four
-      // MFMAs ahead in rotating registers ----
-      {
+      // O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four MFMAs
+      // ahead in rotating registers; piece(i) runs after MFMA i
+      auto value_product = [&](const uint8_t* Zv, const bf16x8* pb, auto piece)
+          __attribute__((always_inline)) {
         constexpr int kAhead = 4;
         bf16x8 vb[kAhead];
         auto vload = [&](int i) __attribute__((always_inline)) {
           const int md = i >> 1, ks = i & 1;
-          const bf16x4 a0 = ds_read_tr16(Z + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
-          const bf16x4 a1 = ds_read_tr16(Z + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
+          const bf16x4 a0 = ds_read_tr16(Zv + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
+          const bf16x4 a1 = ds_read_tr16(Zv + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
           return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         };
 #pragma unroll
@@ -563,13 +571,244 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         for (int i = 0; i < 32; ++i) {
           o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
           if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
+          piece(i);
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if constexpr (kFp8)
-        if (t + 1 < ntiles) widen_own(t + 1, min(2, ntiles - 2 - t));
-    }
+      };
+      // softmax of one tile's scores in pieces: 0, 1 the tile maximum, 2 the
+      // reference, 4, 6, .., 18 two probabilities each, 20 the row sum
+      float tmax = -INFINITY, neg_m = 0.f, psum = 0.f;
+      uint32_t pw[8];
+      auto softmax_piece = [&](const f32x16& sc, int i, bool first) __attribute__((always_inline)) {
+        if (i == 0) {
+          tmax = sc[0];
+#pragma unroll
+          for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, sc[k]);
+        } else if (i == 1) {
+#pragma unroll
+          for (int k = 8; k < 16; ++k) tmax = fmaxf(tmax, sc[k]);
+        } else if (i == 2) {
+          const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
+          m_seen = fmaxf(m_seen, mt);
+          if (first) m_ref = mt;  // the segment's first tile
+          halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
+          neg_m = -m_ref;
+          psum = 0.f;
+        } else if (i >= 4 && i <= 18 && (i & 1) == 0) {
+          const int j = (i - 4) >> 1;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j], sl2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j + 1], sl2, neg_m));
+          psum += p0 + p1;
+          pw[j] = pack_bf16x2(p0, p1);
+        } else if (i == 20) {
+          l_run += sum_with_lane32(psum);
+        }
+      };
+      // the probabilities of the tile whose softmax ran last, as the B operand
+      bf16x8 pprev[2];
+      auto take_probs = [&]() __attribute__((always_inline)) {
+        pprev[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        pprev[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+      };
 
+      // wait for tile t, publish it, send tile t+2's loads, compute and mask
+      // tile t's scores
+      auto front = [&](int t) __attribute__((always_inline)) {
+        // this wave's loads of tile t are done (those of tile t+1 may not be)
+        if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        static_assert(kZLoadsPerWave == 9, "wait counts");
+        // tile t is in place for every wave; every wave is done with tile
+        // t-2, whose stage receives tile t+2
+        __syncthreads();
+        const bool spread = t + 2 < ntiles && one_piece(t + 2);
+        const void* sbn = cache;
+        if (spread) sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 2) * kDecBN) * kZRowB);
+        else if (t + 2 < ntiles) issue(t + 2);
+        const uint32_t nbase = lds0 + ((t + 2) % 4) * kZStageB;
+        const uint8_t* Z = sZ + (t % 4) * kZStageB;
+        const int kt = kt0 + t * kDecBN;
+        f32x16 s = spread ? scores_t(Z, sbn, nbase, std::integral_constant<bool, true>())
+                          : scores_t(Z, sbn, nbase, std::integral_constant<bool, false>());
+        // register i holds tile row 16*(i/8) + 8*hf + i%8
+        if (kt < k0 || kt + kDecBN > k1) {
+          const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = (i >> 3) * 16 + (i & 7);
+            if (c < lo || c >= hi) s[i] = -INFINITY;
+          }
+        }
+        return s;
+      };
+      {
+        const f32x16 s = front(0);
+#pragma unroll
+        for (int i = 0; i <= 20; ++i) softmax_piece(s, i, true);
+        take_probs();
+      }
+      for (int t = 1; t < ntiles; ++t) {
+        const f32x16 s = front(t);
+        value_product(sZ + ((t - 1) % 4) * kZStageB, pprev,
+                      [&](int i) __attribute__((always_inline)) { softmax_piece(s, i, false); });
+        take_probs();
+      }
+      value_product(sZ + ((ntiles - 1) % 4) * kZStageB, pprev,
+                    [&](int) __attribute__((always_inline)) {});
+    } else {
+      for (int t = 0; t < min(3, ntiles); ++t) issue(t);
+      // e4m3: each wave waits for its own loads of tile tt and widens exactly
+      // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
+      // one row) into bf16 stage tt % 2; the barrier at the top of the tile
+      // loop then publishes the whole tile. later: tiles issued after tt whose
+      // loads may stay in flight.
+      auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
+        if (later == 2) {
+          if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else if (later == 1) {
+          if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const uint8_t* F = sZ + kStage0 + (tt % 4) * kF8StageB;
+        uint8_t* D = sZ + (tt % 2) * kZStageB;
+  #pragma unroll
+        for (int j = 0; j < kF8LoadsPerWave; ++j) {
+          const int p = wave + kDecWaves * j;
+          if (p < kF8Loads) {
+            const int byte = p * 1024 + lane * 16;
+            const int r = byte / kF8RowB;
+            const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
+            const u32x4 v = *(const u32x4*)(F + byte);
+            *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
+            *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
+          }
+        }
+      };
+      if constexpr (kFp8) widen_own(0, min(2, ntiles - 1));
+
+      for (int t = 0; t < ntiles; ++t) {
+        // wait for this wave's loads of tile t; those of the (at most two) later
+        // tiles already issued may stay in flight
+        if constexpr (!kFp8) {
+          const int later = min(2, ntiles - 1 - t);
+          if (later == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+          else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+          else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
+        // tile t is in place for every wave (bf16: landed; e4m3: widened); every
+        // wave is done with tile t-1, whose stage receives tile t+3 (e4m3: its
+        // bf16 stage receives tile t+1 at the end of this iteration)
+        __syncthreads();
+        // bf16: tile t+3's loads are spread between the score MFMAs below when
+        // it comes in one piece; e4m3 (five loads a wave) issues them at once
+        const bool spread = !kFp8 && t + 3 < ntiles && one_piece(t + 3);
+        const void* sbn = cache;
+        if (spread) {
+          sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 3) * kDecBN) *
+                                          (kFp8 ? kF8RowB : kZRowB));
+        } else if (t + 3 < ntiles) {
+          issue(t + 3);
+        }
+        const uint32_t nbase = lds0 + kStage0 + ((t + 3) % 4) * kStageB;
+        const uint8_t* Z = sZ + (kFp8 ? (t % 2) : (t % 4)) * kZStageB;
+        const int kt = kt0 + t * kDecBN;
+
+        // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
+        auto scores = [&](auto with_dma) __attribute__((always_inline)) {
+          f32x16 sa, sb;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) { sa[i] = 0.f; sb[i] = 0.f; }
+          constexpr int kAhead = 4;
+          constexpr int kEvery = kFp8 ? 8 : 4;  // one load per 4 (e4m3: 8) score steps
+          bf16x8 zb[kAhead];
+          auto zload = [&](int ks) __attribute__((always_inline)) {
+            return *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
+          };
+  #pragma unroll
+          for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
+  #pragma unroll
+          for (int ks = 0; ks < kQSteps; ++ks) {
+            if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sb, 0, 0, 0);
+            else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sa, 0, 0, 0);
+            if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
+            if constexpr (decltype(with_dma)::value) {
+              if (ks % kEvery == 0 && ks / kEvery < kLoadsPerWave) {
+                const int j = ks / kEvery;
+                if (!kFp8 || j < kLoadsPerWave - 1 || wave + kDecWaves * j < kF8Loads)
+                  dma16_s_nb(sbn, dma_off(j), nbase + (wave + kDecWaves * j) * 1024);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) sa[i] += sb[i];
+          return sa;
+        };
+        f32x16 s = spread ? scores(std::integral_constant<bool, true>())
+                          : scores(std::integral_constant<bool, false>());
+
+        // register i holds tile row 16*(i/8) + 8*hf + i%8
+        if (kt < k0 || kt + kDecBN > k1) {
+          const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = (i >> 3) * 16 + (i & 7);
+            if (c < lo || c >= hi) s[i] = -INFINITY;
+          }
+        }
+        float tmax = -INFINITY;
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+        const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
+        m_seen = fmaxf(m_seen, mt);
+        if (t == 0) m_ref = mt;
+        halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
+        const float neg_m = -m_ref;
+        float psum = 0.f;
+        bf16x8 pb[2];
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 wv;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j], sl2, neg_m));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j + 1], sl2, neg_m));
+            psum += p0 + p1;
+            wv[j] = pack_bf16x2(p0, p1);
+          }
+          pb[ks] = __builtin_bit_cast(bf16x8, wv);
+        }
+        l_run += sum_with_lane32(psum);
+
+        // ---- O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four
+        // MFMAs ahead in rotating registers ----
+        {
+          constexpr int kAhead = 4;
+          bf16x8 vb[kAhead];
+          auto vload = [&](int i) __attribute__((always_inline)) {
+            const int md = i >> 1, ks = i & 1;
+            const bf16x4 a0 = ds_read_tr16(Z + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
+            const bf16x4 a1 = ds_read_tr16(Z + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
+            return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          };
+  #pragma unroll
+          for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
+  #pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
+            if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if constexpr (kFp8)
+          if (t + 1 < ntiles) widen_own(t + 1, min(2, ntiles - 2 - t));
+      }
+
+    }
     // partial state of (w, b): slot w + b. The output is stored by groups of
     // eight dims, [slot][dim / 8][head][dim % 8], so that every store
     // instruction writes 1 KB in one piece (32 heads x 32 bytes).
@@ -598,73 +837,6 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
   }
 }
 
-// ---------------------------------------------------------------------------
-// prefix sums of the context lengths (one workgroup)
-// ---------------------------------------------------------------------------
-// The context length of sequence b is ctx[b] + add (add is 1 when ctx holds
-// cache lengths that exclude the new token). Lengths above max_ctx (the
-// host's bound, which sized the ranges) are taken as max_ctx, so the prefix
-// sums stay below 2^31 whatever the device holds; the results of such
-// sequences are unspecified, their reads in bounds.
-__global__ void __launch_bounds__(256) decode_prefix_kernel(uint32_t* cum, const uint32_t* ctx,
-                                                            uint32_t add, int B, uint32_t max_ctx,
-                                                            uint32_t* wstart, int2* wspan,
-                                                            int32_t* wfirst, int G) {
-  __shared__ uint32_t s_scan[256];
-  __shared__ uint32_t s_carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 256) {
-    const int b = base + tid;
-    const uint32_t v = b < B ? (uint32_t)min((uint64_t)ctx[b] + add, (uint64_t)max_ctx) : 0u;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-      const uint32_t x = tid >= d ? s_scan[tid - d] : 0u;
-      __syncthreads();
-      s_scan[tid] += x;
-      __syncthreads();
-    }
-    if (b < B) cum[b + 1] = s_carry + s_scan[tid];
-    __syncthreads();
-    if (tid == 255) s_carry += s_scan[255];
-    __syncthreads();
-  }
-  if (tid == 0) cum[0] = 0;
-  // key range w covers keys [wstart[w], wstart[w+1])
-  const uint32_t N = s_carry;
-  for (int w = tid; w <= G; w += 256) wstart[w] = (uint32_t)(((uint64_t)w * N) / G);
-  __threadfence();  // other threads of the workgroup read these entries below
-  __syncthreads();
-  // first sequence of every key range: largest b with cum[b] <= wstart[w]
-  for (int w = tid; w < G; w += 256) {
-    const uint32_t key = wstart[w];
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cum[mid] <= key) lo = mid; else hi = mid - 1;
-    }
-    wfirst[w] = lo;
-  }
-  // ranges holding sequence b's first and last keys (empty sequences: (0, -1))
-  for (int b = tid; b < B; b += 256) {
-    const uint32_t lo_key = cum[b], hi_key = cum[b + 1];
-    if (hi_key <= lo_key) { wspan[b] = make_int2(0, -1); continue; }
-    int lo = 0, hi = G - 1;  // largest w with wstart[w] <= lo_key
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (wstart[mid] <= lo_key) lo = mid; else hi = mid - 1;
-    }
-    const int w_lo = lo;
-    hi = G - 1;              // largest w with wstart[w] < hi_key
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (wstart[mid] < hi_key) lo = mid; else hi = mid - 1;
-    }
-    wspan[b] = make_int2(w_lo, lo);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // 3. combine the partial states: o_lat[b, h, :] (bf16 hi + lo)
@@ -795,17 +967,9 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16_t* w_uk, int B,
-                                int H, hipStream_t stream) {
-  const dim3 grid(kLora / 128, H, (B + 63) / 64);
-  hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), 0, stream, q_abs, q, w_uk, B, H);
-  return hipGetLastError();
-}
-
-hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, uint32_t add, int B,
-                                int max_ctx, uint32_t* wstart, int2* wspan, int32_t* wfirst,
-                                int G, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(256), 0, stream, cum, ctx, add, B,
-                     (uint32_t)max_ctx, wstart, wspan, wfirst, G);
+                                int H, const PrefixArgs& pa, hipStream_t stream) {
+  const dim3 grid(kLora / 128 + 1, H, (B + 63) / 64);
+  hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), 0, stream, q_abs, q, w_uk, B, H, pa);
   return hipGetLastError();
 }
 

@@ -95,13 +95,23 @@ hipError_t launch_up_project(const GemmArgs&, bool, hipStream_t);
 int attn_num_slots(int B, int total_q);
 hipError_t launch_attn_schedule(int2*, const uint32_t*, int, int, hipStream_t);
 hipError_t launch_prefill_attn(const AttnArgs&, bool, hipStream_t);
+// split-KV range tables: cum [B+1], wstart [G+1], wspan [B], wfirst [G] from the
+// context lengths min(ctx[b] + add, max_ctx)
+struct PrefixArgs {
+  uint32_t* cum;
+  const uint32_t* ctx;
+  uint32_t add;
+  int B;
+  uint32_t max_ctx;
+  uint32_t* wstart;
+  int2* wspan;
+  int32_t* wfirst;
+  int G;
+};
+// q_abs, and the range tables in one extra workgroup
 hipError_t launch_decode_absorb(uint16_t*, const uint16_t*, const uint16_t*, int, int,
-                                hipStream_t);
+                                const PrefixArgs&, hipStream_t);
 hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
-// context length of sequence b: min(ctx[b] + add, max_ctx)
-hipError_t launch_decode_prefix(uint32_t* cum, const uint32_t* ctx, uint32_t add, int B,
-                                int max_ctx, uint32_t* wstart, int2* wspan, int32_t* wfirst,
-                                int G, hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);
