@@ -800,3 +800,16 @@ def test_unified_prefill_with_its_plan_replays_from_a_captured_graph(B):
                                            dec.gamma, dec.freqs, wl.scale, wl.eps,
                                            int(wl.new_lens.max()))
             _assert_close(_f64(got), ref, BF16_MAX, BF16_MEAN)
+
+
+def test_decode_many_sequences_ragged_batch(B):
+    # 130 sequences: three 64-sequence blocks of the absorb grid (the last one
+    # ragged), prefix sums over more than one 256-entry scan block of ranges
+    # when the partition count is raised, contexts from 1 to 300 keys
+    rng = np.random.default_rng(121)
+    ctx = rng.integers(1, 301, size=130)
+    ctx[[0, 64, 129]] = [1, 300, 2]
+    wl = make_decode("many", 122, list(ctx), 4, 16)
+    _say("decode 130 sequences")
+    for parts in (0, 300):
+        _assert_close(_run_decode(B, wl, parts), oracle.decode(wl), BF16_MAX, BF16_MEAN)
