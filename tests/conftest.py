@@ -23,6 +23,6 @@ def gpu_available() -> bool:
 
 @pytest.fixture(scope="session")
 def lib():
-    """The HIP library through its Python binding; on a GPU machine it must load."""
+    """The HIP library through its Python binding; where a GPU is present it must load."""
     from mla_chunked_prefill_amd import binding
     return binding.load()
