@@ -300,7 +300,7 @@ int mla_prefill(void* output, const void* q, int32_t dtype,
  * num_partitions equal key ranges, one workgroup each (0 = one per compute
  * unit); ranges that span sequences produce one partial state per sequence,
  * merged by log-sum-exp. The library raises the count when a range would span
- * more than 510 pages. The workspace size depends on all of its arguments.
+ * more than 1022 pages. The workspace size depends on all of its arguments.
  *
  *   output     bf16 [batch_size, num_heads, 128]
  *   q          bf16 [batch_size, num_heads, 192]

@@ -449,18 +449,22 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    // the segment's page-table entries, staged in LDS once
-    int pg[kPTWindow / kDecThreads];
-#pragma unroll
-    for (int i = 0; i < kPTWindow / kDecThreads; ++i) {
-      const int e = tid + kDecThreads * i;
+    // the segment's page-table entries, staged in LDS once: the first two per
+    // thread are loaded before the barrier, the rest after it (registers)
+    auto pt_entry = [&](int e) __attribute__((always_inline)) {
       const int lp = lp0 + e;
-      pg[i] = (e < npg && lp < a.maxp) ? a.page_table[(size_t)b * a.maxp + lp] : 0;
-    }
+      const int v = (e < npg && lp < a.maxp) ? a.page_table[(size_t)b * a.maxp + lp] : 0;
+      return (v < 0 || v >= a.num_pages) ? 0 : v;
+    };
+    int pg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pg[i] = pt_entry(tid + kDecThreads * i);
     __syncthreads();  // the previous segment is done with the page window and the stages
 #pragma unroll
-    for (int i = 0; i < kPTWindow / kDecThreads; ++i)
-      sPT[tid + kDecThreads * i] = (pg[i] < 0 || pg[i] >= a.num_pages) ? 0 : pg[i];
+    for (int i = 0; i < 2; ++i) sPT[tid + kDecThreads * i] = pg[i];
+#pragma unroll
+    for (int i = 2; i < kPTWindow / kDecThreads; ++i)
+      sPT[tid + kDecThreads * i] = pt_entry(tid + kDecThreads * i);
     __syncthreads();  // page window written
     // wait for q here, before any tile load is in flight: the compiler cannot
     // count the tile loads, so a wait it placed for q inside the tile loop

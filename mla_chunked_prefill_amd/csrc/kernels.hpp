@@ -57,7 +57,7 @@ struct AttnArgs {
 };
 // Page-table entries the split-KV kernel stages in LDS per segment; the host
 // sizes key ranges so that a segment never spans more pages.
-constexpr int kDecPageWindow = 512;
+constexpr int kDecPageWindow = 1024;
 struct DecodeArgs {
   const uint16_t* q_abs;     // [B][H][576] bf16
   const void* cache;         // [num_pages][ps][576] bf16 or e4m3fn
