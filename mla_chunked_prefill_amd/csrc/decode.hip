@@ -849,7 +849,6 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 // over the partials first, then their weighted sum. Thousands of independent
 // waves keep many loads in flight. o_lat is written as a bf16 pair (hi, lo)
 // so that the projection, on bf16 MFMA, sees it unrounded to 8 bits.
-constexpr int kCmbHeads = 4;  // heads (waves) per workgroup
 
 // Recompute, in one wave, the partial of (range w, sequence b, head h) against
 // the exact maximum m (log2 domain) the split kernel recorded: plain fp32,
@@ -895,10 +894,9 @@ __device__ void recompute_partial(const CombineArgs& c, int w, int b, int h, flo
   }
 }
 
-__global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineArgs c) {
-  const int b = blockIdx.x;
-  const int h = blockIdx.y * kCmbHeads + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// One wave merges all 512 dims of (sequence b, head h), recomputing marked
+// partials: the path taken when any partial of the workgroup's heads is marked.
+__device__ void combine_head(const CombineArgs& c, int b, int h, int lane) {
   if (h >= c.H) return;
   const int2 span = c.wspan[b];
   float acc[8];
@@ -967,6 +965,96 @@ __global__ void __launch_bounds__(64 * kCmbHeads) decode_combine_kernel(CombineA
   *(u32x4*)(orow + kLora + 8 * lane) = lo;
 }
 
+// Grid (B, ceil(H / 32), 4): a workgroup merges the partials of sequence b
+// for 32 heads and a quarter of the 512 dims. The partial outputs are stored
+// [slot][dim / 8][head][dim % 8], so lane (head = lane / 2, half = lane % 2)
+// of a wave reading one group of eight dims for 32 heads reads 1 KB in one
+// piece. First the per-head maximum over the partials (eight range lanes per
+// head, reduced through LDS); if any partial of these heads is marked, the
+// workgroup of quarter 0 merges them one head per wave with recomputation.
+__global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
+  __shared__ float s_m[8][32];
+  const int b = blockIdx.x;
+  const int hb = blockIdx.y * 32;
+  const int gq = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int2 span = c.wspan[b];
+  {
+    const int hh = tid & 31, wi = tid >> 5;
+    const int h1 = hb + hh;
+    float M = -INFINITY;
+    bool marked = false;
+    if (h1 < c.H) {
+      for (int w = span.x + wi; w <= span.y; w += 8) {
+        if (c.wstart[w] < c.wstart[w + 1]) {  // empty range: no partial
+          const float* ml = c.part_ml + ((size_t)(w + b) * c.H + h1) * 2;
+          M = fmaxf(M, ml[0]);
+          marked = marked || ml[1] < 0.f;
+        }
+      }
+    }
+    s_m[wi][hh] = M;
+    if (__syncthreads_or(marked)) {
+      if (gq == 0)
+        for (int k = wave; k < 32; k += 4) combine_head(c, b, hb + k, lane);
+      return;
+    }
+  }
+  const int hl = lane >> 1, half = lane & 1;
+  const int head = hb + hl;
+  if (head >= c.H) return;
+  float Mh = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) Mh = fmaxf(Mh, s_m[j][hl]);
+  const int g0 = gq * 16 + wave * 4;  // this wave's four groups of eight dims
+  float acc[4][4];
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[gg][e] = 0.f;
+  if (span.y >= span.x) {
+    float L = 0.f;
+    for (int w = span.x; w <= span.y; ++w) {
+      if (!(c.wstart[w] < c.wstart[w + 1])) continue;
+      const size_t slot = (size_t)(w + b);
+      const float* ml = c.part_ml + (slot * c.H + head) * 2;
+      const float m = ml[0], l = ml[1];
+      f32x4 v[4];
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        v[gg] = *(const f32x4*)(c.part_o + ((slot * (kLora / 8) + g0 + gg) * c.H + head) * 8 +
+                                half * 4);
+      const float wt = __builtin_amdgcn_exp2f(m - Mh);
+      L += wt * l;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[gg][e] = fmaf(wt, v[gg][e], acc[gg][e]);
+    }
+    // a sink adds e^sink to the denominator (L and acc are relative to 2^Mh)
+    if (c.sink) L += __builtin_amdgcn_exp2f(c.sink[b] * 1.44269504088896341f - Mh);
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[gg][e] *= inv;
+  }
+  uint16_t* orow = c.o_lat + ((size_t)b * c.H + head) * (2 * kLora);
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    u32x2 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      hi[j] = pack_bf16x2(acc[gg][2 * j], acc[gg][2 * j + 1]);
+      lo[j] = pack_bf16x2(acc[gg][2 * j] - bf16_lo(hi[j]), acc[gg][2 * j + 1] - bf16_hi(hi[j]));
+    }
+    const int d = (g0 + gg) * 8 + half * 4;
+    *(u32x2*)(orow + d) = hi;
+    *(u32x2*)(orow + kLora + d) = lo;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -986,8 +1074,8 @@ hipError_t launch_decode_split(const DecodeArgs& a, bool fp8, hipStream_t stream
 }
 
 hipError_t launch_decode_combine(const CombineArgs& c, hipStream_t stream) {
-  const dim3 grid(c.B, (c.H + kCmbHeads - 1) / kCmbHeads);
-  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(64 * kCmbHeads), 0, stream, c);
+  const dim3 grid(c.B, (c.H + 31) / 32, 4);
+  hipLaunchKernelGGL(decode_combine_kernel, grid, dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 
