@@ -270,23 +270,21 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
 // against their exact maximum.
 //
 // Tiles are aligned to 32 keys of the sequence (keys of the first tile before
-// the range start are masked), one barrier per tile, four LDS stages. bf16:
-// a wave computes tile t's scores, then tile t-1's value product with tile
-// t's softmax placed between its MFMAs (those MFMAs wait on LDS reads, which
-// leaves room for the vector work); the stages hold tiles t-1 .. t+2 and the
-// loads of tile t+2 go out while tile t's scores are computed. e4m3: each
-// tile's scores, softmax and value product in turn, the stages holding tiles
-// t .. t+3, loads three tiles ahead. When the page size is a multiple of 32 a tile is 32
+// the range start are masked), one barrier per tile. A wave computes tile
+// t's scores, then tile t-1's value product with tile t's softmax placed
+// between its MFMAs (those MFMAs wait on LDS reads, which leaves room for the
+// vector work); the loads of tile t+2 go out while tile t's scores are
+// computed. bf16: four stages hold tiles t-1 .. t+2. When the page size is a multiple of 32 a tile is 32
 // consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its direct
 // loads are spread between the score MFMAs; otherwise every row's pool slot
 // is looked up and the loads go out in one burst. A bf16 row keeps its 72
 // 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
 // the score reads (16 rows at one column) and the transposed reads (4 rows x
 // 64 bytes) touch distinct LDS banks. An e4m3 tile lands, rows as stored, in
-// one of four staging buffers; once the value product of the tile before it
-// is issued, every wave widens exactly the bytes its own loads brought into
-// the other of two bf16 stages, so the one barrier per tile also publishes
-// the widened tile.
+// one of two load stages; at the end of iteration t every wave widens
+// exactly the bytes its own loads of tile t+1 brought into the third of
+// three bf16 stages (the other two hold tiles t-1 and t), so the one barrier
+// per tile also publishes the widened tile.
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBN = 32;                          // keys per tile
@@ -302,12 +300,13 @@ constexpr float kDecSlack = 64.0f;
 // e4m3 cache: rows kept as stored in the staging buffers
 constexpr int kF8RowB = kCache;                     // 576 bytes
 constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
-constexpr int kF8Stages = 4;
+constexpr int kF8Stages = 2;                        // e4m3 tiles as stored
+constexpr int kZStagesF8 = 3;                       // e4m3: bf16 stages the tiles are widened into
 constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
 constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 5 (waves 2, 3: 4)
 static_assert(kZLoads % kDecWaves == 0, "even bf16 loads per wave");
 static_assert(kF8Loads == 4 * kDecWaves + 2, "e4m3: waves 0, 1 load five times, waves 2, 3 four");
-static_assert(2 * kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
+static_assert(kZStagesF8 * kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
 static_assert(kPTWindow % kDecThreads == 0, "even page-table staging per thread");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
@@ -369,7 +368,9 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
   __shared__ int sPT[kPTWindow];
   constexpr int kLoadsPerWave = kFp8 ? kF8LoadsPerWave : kZLoadsPerWave;
   constexpr int kStageB = kFp8 ? kF8StageB : kZStageB;
-  constexpr int kStage0 = kFp8 ? 2 * kZStageB : 0;    // byte offset of load stage 0
+  constexpr int kStage0 = kFp8 ? kZStagesF8 * kZStageB : 0;  // byte offset of load stage 0
+  constexpr int kLoadStages = kFp8 ? kF8Stages : kZStages;
+  constexpr int kBfStages = kFp8 ? kZStagesF8 : kZStages;
 
   const int w = blockIdx.x;
   if (w >= a.G) return;
@@ -484,7 +485,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     // all loads of tile t into load stage t % 4, in one burst
     auto issue = [&](int t) __attribute__((always_inline)) {
       const int kt = kt0 + t * kDecBN;
-      const uint32_t base = lds0 + kStage0 + (t % 4) * kStageB;
+      const uint32_t base = lds0 + kStage0 + (t % kLoadStages) * kStageB;
       if (one_piece(t)) {
         const void* sb = uniform_ptr_d(cache + (size_t)slot_of(kt) * (kFp8 ? kF8RowB : kZRowB));
 #pragma unroll
@@ -525,294 +526,176 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     float l_run = 0.f;
     bool halted = false;       // wave-uniform: the partial is marked for recomputation
 
-    if constexpr (!kFp8) {
-      // bf16: tile t's scores, then tile t-1's value product with tile t's
-      // softmax interleaved between its MFMAs (the value MFMAs wait on LDS
-      // reads; the softmax fills those gaps). Stages hold tiles t-1 (value
-      // product), t (scores), t+1 and t+2 (loads in flight): the loads of
-      // tile t+2 go out once the barrier of tile t shows every wave done
-      // with tile t-2.
-      for (int t = 0; t < min(2, ntiles); ++t) issue(t);
-      auto scores_t = [&](const uint8_t* Zs, const void* sbn, uint32_t nbase, auto with_dma)
-          __attribute__((always_inline)) {
-        f32x16 acc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-        constexpr int kAhead = 4;
-        bf16x8 zb[kAhead];
-        auto zload = [&](int ks) __attribute__((always_inline)) {
-          return *(const bf16x8*)(Zs + s_base[ks & 3] + 128 * (ks >> 2));
-        };
-#pragma unroll
-        for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
-#pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], acc, 0, 0, 0);
-          if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
-          if constexpr (decltype(with_dma)::value) {
-            if (ks % 4 == 0 && ks / 4 < kZLoadsPerWave)
-              dma16_s_nb(sbn, dma_off(ks / 4), nbase + (wave + kDecWaves * (ks / 4)) * 1024);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        return acc;
-      };
-      // O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four MFMAs
-      // ahead in rotating registers; piece(i) runs after MFMA i
-      auto value_product = [&](const uint8_t* Zv, const bf16x8* pb, auto piece)
-          __attribute__((always_inline)) {
-        constexpr int kAhead = 4;
-        bf16x8 vb[kAhead];
-        auto vload = [&](int i) __attribute__((always_inline)) {
-          const int md = i >> 1, ks = i & 1;
-          const bf16x4 a0 = ds_read_tr16(Zv + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
-          const bf16x4 a1 = ds_read_tr16(Zv + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
-          return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
-          if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
-          piece(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      // softmax of one tile's scores in pieces: 0, 1 the tile maximum, 2 the
-      // reference, 4, 6, .., 18 two probabilities each, 20 the row sum
-      float tmax = -INFINITY, neg_m = 0.f, psum = 0.f;
-      uint32_t pw[8];
-      auto softmax_piece = [&](const f32x16& sc, int i, bool first) __attribute__((always_inline)) {
-        if (i == 0) {
-          tmax = sc[0];
-#pragma unroll
-          for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, sc[k]);
-        } else if (i == 1) {
-#pragma unroll
-          for (int k = 8; k < 16; ++k) tmax = fmaxf(tmax, sc[k]);
-        } else if (i == 2) {
-          const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
-          m_seen = fmaxf(m_seen, mt);
-          if (first) m_ref = mt;  // the segment's first tile
-          halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
-          neg_m = -m_ref;
-          psum = 0.f;
-        } else if (i >= 4 && i <= 18 && (i & 1) == 0) {
-          const int j = (i - 4) >> 1;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j], sl2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j + 1], sl2, neg_m));
-          psum += p0 + p1;
-          pw[j] = pack_bf16x2(p0, p1);
-        } else if (i == 20) {
-          l_run += sum_with_lane32(psum);
-        }
-      };
-      // the probabilities of the tile whose softmax ran last, as the B operand
-      bf16x8 pprev[2];
-      auto take_probs = [&]() __attribute__((always_inline)) {
-        pprev[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-        pprev[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
-      };
-
-      // wait for tile t, publish it, send tile t+2's loads, compute and mask
-      // tile t's scores
-      auto front = [&](int t) __attribute__((always_inline)) {
-        // this wave's loads of tile t are done (those of tile t+1 may not be)
-        if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        static_assert(kZLoadsPerWave == 9, "wait counts");
-        // tile t is in place for every wave; every wave is done with tile
-        // t-2, whose stage receives tile t+2
-        __syncthreads();
-        const bool spread = t + 2 < ntiles && one_piece(t + 2);
-        const void* sbn = cache;
-        if (spread) sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 2) * kDecBN) * kZRowB);
-        else if (t + 2 < ntiles) issue(t + 2);
-        const uint32_t nbase = lds0 + ((t + 2) % 4) * kZStageB;
-        const uint8_t* Z = sZ + (t % 4) * kZStageB;
-        const int kt = kt0 + t * kDecBN;
-        f32x16 s = spread ? scores_t(Z, sbn, nbase, std::integral_constant<bool, true>())
-                          : scores_t(Z, sbn, nbase, std::integral_constant<bool, false>());
-        // register i holds tile row 16*(i/8) + 8*hf + i%8
-        if (kt < k0 || kt + kDecBN > k1) {
-          const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = (i >> 3) * 16 + (i & 7);
-            if (c < lo || c >= hi) s[i] = -INFINITY;
-          }
-        }
-        return s;
-      };
-      {
-        const f32x16 s = front(0);
-#pragma unroll
-        for (int i = 0; i <= 20; ++i) softmax_piece(s, i, true);
-        take_probs();
+    // tile t's scores, then tile t-1's value product with tile t's softmax
+    // interleaved between its MFMAs (the value MFMAs wait on LDS reads; the
+    // softmax fills those gaps). bf16 stages hold tiles t-1 (value
+    // product), t (scores), t+1 and t+2 (loads in flight): the loads of
+    // tile t+2 go out once the barrier of tile t shows every wave done
+    // with tile t-2. e4m3: three bf16 stages hold tiles t-1, t and t+1,
+    // the last widened at the end of iteration t from its load stage.
+    for (int t = 0; t < min(2, ntiles); ++t) issue(t);
+    // e4m3: each wave waits for its own loads of tile tt and widens exactly
+    // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
+    // one row) into bf16 stage tt % 3; the barrier at the top of the tile
+    // loop then publishes the whole tile. later: tiles issued after tt whose
+    // loads may stay in flight.
+    auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
+      if (later == 1) {
+        if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      for (int t = 1; t < ntiles; ++t) {
-        const f32x16 s = front(t);
-        value_product(sZ + ((t - 1) % 4) * kZStageB, pprev,
-                      [&](int i) __attribute__((always_inline)) { softmax_piece(s, i, false); });
-        take_probs();
+      const uint8_t* F = sZ + kStage0 + (tt % kF8Stages) * kF8StageB;
+      uint8_t* D = sZ + (tt % kZStagesF8) * kZStageB;
+#pragma unroll
+      for (int j = 0; j < kF8LoadsPerWave; ++j) {
+        const int p = wave + kDecWaves * j;
+        if (p < kF8Loads) {
+          const int byte = p * 1024 + lane * 16;
+          const int r = byte / kF8RowB;
+          const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
+          const u32x4 v = *(const u32x4*)(F + byte);
+          *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
+          *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
+        }
       }
-      value_product(sZ + ((ntiles - 1) % 4) * kZStageB, pprev,
-                    [&](int) __attribute__((always_inline)) {});
-    } else {
-      for (int t = 0; t < min(3, ntiles); ++t) issue(t);
-      // e4m3: each wave waits for its own loads of tile tt and widens exactly
-      // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
-      // one row) into bf16 stage tt % 2; the barrier at the top of the tile
-      // loop then publishes the whole tile. later: tiles issued after tt whose
-      // loads may stay in flight.
-      auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
-        if (later == 2) {
-          if (wave < 2) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-          else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        } else if (later == 1) {
-          if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-          else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        } else {
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        const uint8_t* F = sZ + kStage0 + (tt % 4) * kF8StageB;
-        uint8_t* D = sZ + (tt % 2) * kZStageB;
-  #pragma unroll
-        for (int j = 0; j < kF8LoadsPerWave; ++j) {
-          const int p = wave + kDecWaves * j;
-          if (p < kF8Loads) {
-            const int byte = p * 1024 + lane * 16;
-            const int r = byte / kF8RowB;
-            const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
-            const u32x4 v = *(const u32x4*)(F + byte);
-            *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
-            *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
-          }
-        }
+    };
+    if constexpr (kFp8) widen_own(0, min(1, ntiles - 1));
+    auto scores_t = [&](const uint8_t* Zs, const void* sbn, uint32_t nbase, auto with_dma)
+        __attribute__((always_inline)) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      constexpr int kAhead = 4;
+      bf16x8 zb[kAhead];
+      auto zload = [&](int ks) __attribute__((always_inline)) {
+        return *(const bf16x8*)(Zs + s_base[ks & 3] + 128 * (ks >> 2));
       };
-      if constexpr (kFp8) widen_own(0, min(2, ntiles - 1));
-
-      for (int t = 0; t < ntiles; ++t) {
-        // wait for this wave's loads of tile t; those of the (at most two) later
-        // tiles already issued may stay in flight
-        if constexpr (!kFp8) {
-          const int later = min(2, ntiles - 1 - t);
-          if (later == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-          else if (later == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-          else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], acc, 0, 0, 0);
+        if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
+        if constexpr (decltype(with_dma)::value) {
+          if (ks % 4 == 0 && ks / 4 < kZLoadsPerWave)
+            dma16_s_nb(sbn, dma_off(ks / 4), nbase + (wave + kDecWaves * (ks / 4)) * 1024);
         }
-        static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
-        // tile t is in place for every wave (bf16: landed; e4m3: widened); every
-        // wave is done with tile t-1, whose stage receives tile t+3 (e4m3: its
-        // bf16 stage receives tile t+1 at the end of this iteration)
-        __syncthreads();
-        // bf16: tile t+3's loads are spread between the score MFMAs below when
-        // it comes in one piece; e4m3 (five loads a wave) issues them at once
-        const bool spread = !kFp8 && t + 3 < ntiles && one_piece(t + 3);
-        const void* sbn = cache;
-        if (spread) {
-          sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 3) * kDecBN) *
-                                          (kFp8 ? kF8RowB : kZRowB));
-        } else if (t + 3 < ntiles) {
-          issue(t + 3);
-        }
-        const uint32_t nbase = lds0 + kStage0 + ((t + 3) % 4) * kStageB;
-        const uint8_t* Z = sZ + (kFp8 ? (t % 2) : (t % 4)) * kZStageB;
-        const int kt = kt0 + t * kDecBN;
-
-        // ---- S^T = Z Q^T: 32 keys x 32 heads, two accumulation chains ----
-        auto scores = [&](auto with_dma) __attribute__((always_inline)) {
-          f32x16 sa, sb;
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) { sa[i] = 0.f; sb[i] = 0.f; }
-          constexpr int kAhead = 4;
-          constexpr int kEvery = kFp8 ? 8 : 4;  // one load per 4 (e4m3: 8) score steps
-          bf16x8 zb[kAhead];
-          auto zload = [&](int ks) __attribute__((always_inline)) {
-            return *(const bf16x8*)(Z + s_base[ks & 3] + 128 * (ks >> 2));
-          };
-  #pragma unroll
-          for (int ks = 0; ks < kAhead; ++ks) zb[ks] = zload(ks);
-  #pragma unroll
-          for (int ks = 0; ks < kQSteps; ++ks) {
-            if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sb, 0, 0, 0);
-            else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb[ks % kAhead], qf[ks], sa, 0, 0, 0);
-            if (ks + kAhead < kQSteps) zb[ks % kAhead] = zload(ks + kAhead);
-            if constexpr (decltype(with_dma)::value) {
-              if (ks % kEvery == 0 && ks / kEvery < kLoadsPerWave) {
-                const int j = ks / kEvery;
-                if (!kFp8 || j < kLoadsPerWave - 1 || wave + kDecWaves * j < kF8Loads)
-                  dma16_s_nb(sbn, dma_off(j), nbase + (wave + kDecWaves * j) * 1024);
-              }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) sa[i] += sb[i];
-          return sa;
-        };
-        f32x16 s = spread ? scores(std::integral_constant<bool, true>())
-                          : scores(std::integral_constant<bool, false>());
-
-        // register i holds tile row 16*(i/8) + 8*hf + i%8
-        if (kt < k0 || kt + kDecBN > k1) {
-          const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
-  #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int c = (i >> 3) * 16 + (i & 7);
-            if (c < lo || c >= hi) s[i] = -INFINITY;
-          }
-        }
-        float tmax = -INFINITY;
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return acc;
+    };
+    // O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four MFMAs
+    // ahead in rotating registers; piece(i) runs after MFMA i
+    auto value_product = [&](const uint8_t* Zv, const bf16x8* pb, auto piece)
+        __attribute__((always_inline)) {
+      constexpr int kAhead = 4;
+      bf16x8 vb[kAhead];
+      auto vload = [&](int i) __attribute__((always_inline)) {
+        const int md = i >> 1, ks = i & 1;
+        const bf16x4 a0 = ds_read_tr16(Zv + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
+        const bf16x4 a1 = ds_read_tr16(Zv + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
+        return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
+        if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
+        piece(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // softmax of one tile's scores in pieces: 0, 1 the tile maximum, 2 the
+    // reference, 4, 6, .., 18 two probabilities each, 20 the row sum
+    float tmax = -INFINITY, neg_m = 0.f, psum = 0.f;
+    uint32_t pw[8];
+    auto softmax_piece = [&](const f32x16& sc, int i, bool first) __attribute__((always_inline)) {
+      if (i == 0) {
+        tmax = sc[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) tmax = fmaxf(tmax, sc[k]);
+      } else if (i == 1) {
+#pragma unroll
+        for (int k = 8; k < 16; ++k) tmax = fmaxf(tmax, sc[k]);
+      } else if (i == 2) {
         const float mt = max_with_lane32(tmax) * sl2;  // finite: every tile holds a valid key
         m_seen = fmaxf(m_seen, mt);
-        if (t == 0) m_ref = mt;
+        if (first) m_ref = mt;  // the segment's first tile
         halted = halted || (__ballot(mt > m_ref + kDecSlack) != 0);
-        const float neg_m = -m_ref;
-        float psum = 0.f;
-        bf16x8 pb[2];
-  #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          u32x4 wv;
-  #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j], sl2, neg_m));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks * 8 + 2 * j + 1], sl2, neg_m));
-            psum += p0 + p1;
-            wv[j] = pack_bf16x2(p0, p1);
-          }
-          pb[ks] = __builtin_bit_cast(bf16x8, wv);
-        }
+        neg_m = -m_ref;
+        psum = 0.f;
+      } else if (i >= 4 && i <= 18 && (i & 1) == 0) {
+        const int j = (i - 4) >> 1;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j], sl2, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[2 * j + 1], sl2, neg_m));
+        psum += p0 + p1;
+        pw[j] = pack_bf16x2(p0, p1);
+      } else if (i == 20) {
         l_run += sum_with_lane32(psum);
-
-        // ---- O^T[512 dims x 32 heads] += Z^T P^T, transposed fragments four
-        // MFMAs ahead in rotating registers ----
-        {
-          constexpr int kAhead = 4;
-          bf16x8 vb[kAhead];
-          auto vload = [&](int i) __attribute__((always_inline)) {
-            const int md = i >> 1, ks = i & 1;
-            const bf16x4 a0 = ds_read_tr16(Z + tr_base[0][md & 1] + 18432 * ks + 128 * (md >> 1));
-            const bf16x4 a1 = ds_read_tr16(Z + tr_base[1][md & 1] + 18432 * ks + 128 * (md >> 1));
-            return __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          };
-  #pragma unroll
-          for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
-  #pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            o[i >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i % kAhead], pb[i & 1], o[i >> 1], 0, 0, 0);
-            if (i + kAhead < 32) vb[i % kAhead] = vload(i + kAhead);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        if constexpr (kFp8)
-          if (t + 1 < ntiles) widen_own(t + 1, min(2, ntiles - 2 - t));
       }
+    };
+    // the probabilities of the tile whose softmax ran last, as the B operand
+    bf16x8 pprev[2];
+    auto take_probs = [&]() __attribute__((always_inline)) {
+      pprev[0] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pprev[1] = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    };
 
+    // wait for tile t, publish it, send tile t+2's loads, compute and mask
+    // tile t's scores
+    auto front = [&](int t) __attribute__((always_inline)) {
+      // this wave's loads of tile t are done (those of tile t+1 may not be;
+      // e4m3: the wave widened its part of tile t already)
+      if constexpr (!kFp8) {
+        if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
+      // tile t is in place for every wave; every wave is done with tile
+      // t-2, whose stage receives tile t+2 (e4m3: with tile t, whose load
+      // stage receives tile t+2)
+      __syncthreads();
+      const bool spread = !kFp8 && t + 2 < ntiles && one_piece(t + 2);
+      const void* sbn = cache;
+      if (spread) sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 2) * kDecBN) * kZRowB);
+      else if (t + 2 < ntiles) issue(t + 2);
+      const uint32_t nbase = lds0 + ((t + 2) % 4) * kZStageB;
+      const uint8_t* Z = sZ + (t % kBfStages) * kZStageB;
+      const int kt = kt0 + t * kDecBN;
+      f32x16 s = spread ? scores_t(Z, sbn, nbase, std::integral_constant<bool, true>())
+                        : scores_t(Z, sbn, nbase, std::integral_constant<bool, false>());
+      // register i holds tile row 16*(i/8) + 8*hf + i%8
+      if (kt < k0 || kt + kDecBN > k1) {
+        const int lo = k0 - kt - hf * 8, hi = k1 - kt - hf * 8;  // valid: lo <= c < hi
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = (i >> 3) * 16 + (i & 7);
+          if (c < lo || c >= hi) s[i] = -INFINITY;
+        }
+      }
+      return s;
+    };
+    {
+      const f32x16 s = front(0);
+#pragma unroll
+      for (int i = 0; i <= 20; ++i) softmax_piece(s, i, true);
+      take_probs();
+      if constexpr (kFp8)
+        if (1 < ntiles) widen_own(1, min(1, ntiles - 2));
     }
+    for (int t = 1; t < ntiles; ++t) {
+      const f32x16 s = front(t);
+      value_product(sZ + ((t - 1) % kBfStages) * kZStageB, pprev,
+                    [&](int i) __attribute__((always_inline)) { softmax_piece(s, i, false); });
+      take_probs();
+      if constexpr (kFp8)
+        if (t + 1 < ntiles) widen_own(t + 1, min(1, ntiles - 2 - t));
+    }
+    value_product(sZ + ((ntiles - 1) % kBfStages) * kZStageB, pprev,
+                  [&](int) __attribute__((always_inline)) {});
     // partial state of (w, b): slot w + b. The output is stored by groups of
     // eight dims, [slot][dim / 8][head][dim % 8], so that every store
     // instruction writes 1 KB in one piece (32 heads x 32 bytes).
