@@ -363,7 +363,7 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
 
 template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
-  // bf16: four stages; e4m3: two bf16 stages and four staging buffers behind them
+  // bf16: four stages; e4m3: three bf16 stages and two load stages behind them
   __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
   __shared__ int sPT[kPTWindow];
   constexpr int kLoadsPerWave = kFp8 ? kF8LoadsPerWave : kZLoadsPerWave;
