@@ -10,15 +10,15 @@
 // accumulators live in the accumulation registers, so every operand fragment
 // read from LDS feeds four MFMAs.
 //
-// The 512-long reduction runs in 32-wide slices that go from global memory
+// The 512-long reduction runs in 64-wide slices that go from global memory
 // straight into LDS stages with 16-byte direct loads (global_load_lds_dwordx4);
-// 64-byte LDS rows keep their four 16-byte chunks XORed by (row / 4) % 4 so
-// that 16 consecutive rows read at one column hit distinct banks. The one
-// workgroup barrier per slice sits between the slice's two 16-deep k-steps:
+// 128-byte LDS rows keep their eight 16-byte chunks XORed by (row / 2) % 8 so
+// that the fragment reads (32 rows at one chunk) are conflict-free. The one
+// workgroup barrier per slice sits before the slice's last 16-deep k-step:
 // before it a wave has read all of the slice's fragments and waited for its
 // own loads of the next slice; after it, the next slice's first fragments and
-// a new slice's loads go out while the second k-step's MFMAs run, which
-// hides the latency of those reads behind matrix work.
+// a new slice's loads go out while the last k-step's MFMAs run. (32-wide
+// slices, one barrier per two k-steps, measured 6% slower.)
 //
 // Epilogue: each wave stages its quadrant in LDS in the destination's layout
 // and writes it with 16-byte stores, 1 KB of contiguous memory per
@@ -34,10 +34,10 @@
 namespace mla {
 
 constexpr int kGemmBM = 256;                   // latent rows per workgroup
-constexpr int kGemmBK = 32;                    // reduction slice
+constexpr int kGemmBK = 64;                    // reduction slice
 constexpr int kGemmSlices = kLora / kGemmBK;   // 16
-constexpr int kGemmRowB = kGemmBK * 2;         // 64 bytes per LDS row
-constexpr int kGemmOpB = kGemmBM * kGemmRowB;  // 16 KB per operand and stage
+constexpr int kGemmRowB = kGemmBK * 2;         // 128 bytes per LDS row
+constexpr int kGemmOpB = kGemmBM * kGemmRowB;  // 32 KB per operand and stage
 constexpr int kGemmStageB = 2 * kGemmOpB;      // latent slice, then W slice
 constexpr int kGemmStages = 2;                 // LDS stages (three measured no faster)
 constexpr int kGemmEpiB = 32768;               // per wave in the epilogue
@@ -46,7 +46,7 @@ constexpr int kGemmLdsB =
 static_assert(kGemmStages >= 2 && kGemmStages <= 4, "LDS stages");
 static_assert(kGemmLdsB <= 160 * 1024, "LDS of one CU");
 
-__device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
 // direct global -> LDS load of 16 bytes per lane from sbase + voff (sbase
 // wave-uniform) to lds + 16 lane; ordered by s_waitcnt vmcnt and barriers
@@ -79,16 +79,16 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  // direct loads: load p (of 16) of an operand slice fills LDS rows 16 p ..
-  // 16 p + 15, lane -> row 16 p + lane / 4, LDS chunk lane % 4 holding source
-  // chunk (lane % 4) ^ gswz(row); this wave issues loads p = wave + 4 k
+  // direct loads: load p (of 32) of an operand slice fills LDS rows 8 p ..
+  // 8 p + 7, lane -> row 8 p + lane / 8, LDS chunk lane % 8 holding source
+  // chunk (lane % 8) ^ gswz(row); this wave issues loads p = wave + 4 k
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)smem);
-  uint32_t offA[4], offB[4];  // bytes from the operand bases
+  uint32_t offA[8], offB[8];  // bytes from the operand bases
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 8; ++k) {
     const int p = wave + 4 * k;
-    const int r = 16 * p + (lane >> 2);
-    const int ch = (lane & 3) ^ gswz(r);
+    const int r = 8 * p + (lane >> 3);
+    const int ch = (lane & 7) ^ gswz(r);
     const int arow = min(m0 + r, nvalid - 1);      // past the chunk: a valid row, output zeroed
     const int wrow = r < 128 * n_h ? r : r - 128;  // a lone last head: its own rows again
     offA[k] = (uint32_t)(arow * kLora * 2 + ch * 16);
@@ -99,9 +99,9 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
     const void* sa = g_uniform(g.a + s * kGemmBK);
     const void* sb = g_uniform(W + s * kGemmBK);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) gdma16(sa, offA[k], base + (wave + 4 * k) * 1024);
+    for (int k = 0; k < 8; ++k) gdma16(sa, offA[k], base + (wave + 4 * k) * 1024);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) gdma16(sb, offB[k], base + kGemmOpB + (wave + 4 * k) * 1024);
+    for (int k = 0; k < 8; ++k) gdma16(sb, offB[k], base + kGemmOpB + (wave + 4 * k) * 1024);
   };
 
   f32x16 acc[4][4];
@@ -143,38 +143,39 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
   // fragments read
 #pragma unroll
   for (int s = 0; s < kGemmStages; ++s) issue(s);
-  if (kGemmStages == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (kGemmStages == 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  static_assert(kGemmStages == 2, "wait counts");
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // slice 0 landed, slice 1 may not have
   __syncthreads();
   bf16x8 f0[8], f1[8];
   read(0, 0, f0);
 
-  // Slice s lives in stage s % stages. At the barrier in the middle of slice
-  // s every wave has all of slice s in registers and its own loads of slice
-  // s + 1 landed (loads of later slices may still be in flight): slice s + 1
-  // can be read, and stage s % stages takes slice s + stages. sched_barrier
-  // fences keep each k-step's MFMAs between the waits and barriers that bound
-  // them (MFMAs touch no memory, so the scheduler would otherwise move them).
+  // Slice s lives in stage s % stages and takes four 16-deep k-steps. At the
+  // barrier before its last k-step every wave has all of slice s in
+  // registers and its own loads of slice s + 1 landed: slice s + 1 can be
+  // read, and stage s % stages takes slice s + 2. sched_barrier fences keep
+  // each k-step's MFMAs between the waits and barriers that bound them
+  // (MFMAs touch no memory, so the scheduler would otherwise move them).
 #pragma unroll 1
   for (int s = 0; s < kGemmSlices; ++s) {
     read(s, 1, f1);
     mfmas(f0);  // k-step 0 of slice s
     __builtin_amdgcn_sched_barrier(0);
+    read(s, 2, f0);
+    mfmas(f1);  // k-step 1
+    __builtin_amdgcn_sched_barrier(0);
+    read(s, 3, f1);
+    mfmas(f0);  // k-step 2
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < kGemmSlices) {
-      // slices issued: 0 .. min(s + stages - 1, last); those after s + 1 may
-      // stay in flight, 8 loads each
-      const int later = min(kGemmStages - 2, kGemmSlices - 2 - s);
-      if (later <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else if (later == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      // slice s + 1 is the last one issued: wait for all of this wave's loads
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slice s fully in registers
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       if (s + kGemmStages < kGemmSlices) issue(s + kGemmStages);
       read(s + 1, 0, f0);
     }
-    mfmas(f1);  // k-step 1 of slice s
+    mfmas(f1);  // k-step 3 of slice s
     __builtin_amdgcn_sched_barrier(0);
   }
 
