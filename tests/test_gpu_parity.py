@@ -67,6 +67,17 @@ def test_plan_bit_exact_named(B, name):
     assert g[3] == -(-int((new + cached).max()) // T)
 
 
+def test_plan_golden_worked_example(B):
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "plan_two_sequences.json")))
+    bro, co, bl, need = _plan_gpu(B, g["input_row_offsets"], g["cache_lengths"],
+                                  g["buffer_token_size"], g["max_chunks"])
+    assert bro.tolist() == g["buffer_row_offsets"] and co.tolist() == g["cache_offsets"]
+    assert bl.tolist() == g["buffer_lengths"] and need == g["chunks_needed"]
+
+
 def test_plan_bit_exact_random_and_edges(B):
     rng = np.random.default_rng(123)
     cases = []

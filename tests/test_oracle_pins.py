@@ -7,7 +7,9 @@ oracle's own library routine on the same expression.
 """
 import dataclasses
 import itertools
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -55,13 +57,19 @@ def test_bf16_sample_codes_match_torch():
 # plan (mla_prefill_plan page)
 # ---------------------------------------------------------------------------
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
 def test_plan_worked_example_two_sequences():
-    """Hand-worked from the page's Args definitions: lengths 5 (0 cached) and
+    """Hand-worked from the page's Args definitions (tests/golden/
+    plan_two_sequences.json holds the derivation): lengths 5 (0 cached) and
     18 (7 cached + 11 new), 8-token chunks, 4 chunk slots."""
-    bro, co, bl = oracle.plan([0, 5, 16], [0, 7], 8, 4)
-    assert bro.tolist() == [[0, 5, 13], [0, 0, 8], [0, 0, 2], [0, 0, 0]]
-    assert co.tolist() == [[0, 0], [5, 8], [5, 16], [5, 18]]
-    assert bl.tolist() == [13, 8, 2, -1]
+    g = json.load(open(os.path.join(GOLDEN, "plan_two_sequences.json")))
+    bro, co, bl = oracle.plan(g["input_row_offsets"], g["cache_lengths"],
+                              g["buffer_token_size"], g["max_chunks"])
+    assert bro.tolist() == g["buffer_row_offsets"]
+    assert co.tolist() == g["cache_offsets"]
+    assert bl.tolist() == g["buffer_lengths"]
     assert bro.dtype == np.uint32 and co.dtype == np.uint32 and bl.dtype == np.int32
 
 
