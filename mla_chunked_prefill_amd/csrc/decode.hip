@@ -103,85 +103,101 @@ __device__ void decode_prefix(const PrefixArgs& pa) {
 }
 
 // q_abs[b, h, 0:512] = w_uk[h] q_nope[b, h]; q_abs[b, h, 512:576] = q_rope[b, h].
-// Grid (512 / 128 + 1, H, ceil(B / 64)); wave v of column block x < 4 computes
-// latent dims 128 x + 32 v .. + 31 for 64 sequences (two 32-sequence blocks)
-// as D = W Q^T, so that a lane holds four runs of four consecutive dims of
-// one sequence; an exchange with the lane 32 away turns them into two runs
-// of eight, each stored with one 16-byte store. The workgroups of column
-// block 0 also copy the rope part of their sequences; workgroup (4, 0, 0)
-// computes the split-KV prefix sums, the rest of column 4 exits.
+// Grid (H + 1, ceil(B / 64)): workgroup (h, z) handles head h for sequences
+// 64 z .. 64 z + 63. Their q_nope rows (16 KB) are staged in LDS once, 16-byte
+// chunks XORed by (row % 16) so that 32 rows read at one chunk hit distinct
+// banks; wave v computes latent dims 128 v .. 128 v + 127 (four 32-dim blocks,
+// all w_uk loads issued up front) as D = W Q^T, so that a lane holds four runs
+// of four consecutive dims of one sequence; an exchange with the lane 32 away
+// turns them into two runs of eight, each stored with one 16-byte store. The
+// workgroup also copies the rope part of its sequences. Workgroup (H, 0)
+// computes the split-KV prefix sums; the rest of column H exits.
 __global__ void __launch_bounds__(256) absorb_kernel(uint16_t* __restrict__ q_abs,
                                                      const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ w_uk, int B,
                                                      int H, PrefixArgs pa) {
-  if (blockIdx.x == kLora / 128) {
-    if (blockIdx.y == 0 && blockIdx.z == 0) decode_prefix(pa);
+  if ((int)blockIdx.x == H) {
+    if (blockIdx.y == 0) decode_prefix(pa);
     return;
   }
+  __shared__ __attribute__((aligned(16))) uint8_t sq[64 * 256];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int h = blockIdx.y;
-  const int n0 = blockIdx.x * 128 + wave * 32;
-  const int b0 = blockIdx.z * 64;
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * 64;
   constexpr int kSteps = kNope / 16;  // 8
-  const uint16_t* wp = w_uk + ((size_t)h * kLora + n0 + l32) * kNope + hf * 8;
-  u32x4 wf[kSteps], xf[2][kSteps];
+  // this wave's w_uk rows: four blocks of 32 dims, all loads up front
+  u32x4 wf[4][kSteps];
 #pragma unroll
-  for (int k = 0; k < kSteps; ++k) wf[k] = *(const u32x4*)(wp + 16 * k);
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint16_t* wp = w_uk + ((size_t)h * kLora + wave * 128 + nb * 32 + l32) * kNope + hf * 8;
 #pragma unroll
-  for (int bt = 0; bt < 2; ++bt) {
-    const int brow = b0 + 32 * bt + l32;
-    const uint16_t* xp = q + ((size_t)min(brow, B - 1) * H + h) * kQDepth + hf * 8;
+    for (int k = 0; k < kSteps; ++k) wf[nb][k] = *(const u32x4*)(wp + 16 * k);
+  }
+  // q_nope rows of the 64 sequences: thread t loads row t / 4, chunks 4 (t % 4) ..
+  {
+    const int r = tid >> 2;
+    const int b = min(b0 + r, B - 1);
+    const uint16_t* qp = q + ((size_t)b * H + h) * kQDepth;
 #pragma unroll
-    for (int k = 0; k < kSteps; ++k) {
-      xf[bt][k] = *(const u32x4*)(xp + 16 * k);
-      if (brow >= B) xf[bt][k] = u32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j) {
+      const int c = (tid & 3) * 4 + j;
+      u32x4 v = *(const u32x4*)(qp + c * 8);
+      if (b0 + r >= B) v = u32x4{0, 0, 0, 0};
+      *(u32x4*)(sq + r * 256 + ((c ^ (r & 15)) * 16)) = v;
+    }
+    // the rope part of the same rows: 64 rows x 8 chunks, two per thread
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int piece = j * 256 + tid;
+      const int rr = piece >> 3, c = (piece & 7) * 8;
+      if (b0 + rr < B)
+        *(u32x4*)(q_abs + ((size_t)(b0 + rr) * H + h) * kCache + kLora + c) =
+            *(const u32x4*)(q + ((size_t)(b0 + rr) * H + h) * kQDepth + kNope + c);
     }
   }
+  __syncthreads();
 #pragma unroll
   for (int bt = 0; bt < 2; ++bt) {
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    bf16x8 xf[kSteps];
+    const int r = bt * 32 + l32;
 #pragma unroll
     for (int k = 0; k < kSteps; ++k)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[k]),
-                                                    __builtin_bit_cast(bf16x8, xf[bt][k]), acc,
-                                                    0, 0, 0);
-    // lane holds sequence b0 + 32 bt + l32, dims n0 + 8 (i / 4) + 4 hf + i % 4
-    const int b = b0 + 32 * bt + l32;
+      xf[k] = *(const bf16x8*)(sq + r * 256 + (((2 * k + hf) ^ (r & 15)) * 16));
+    const int b = b0 + r;
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-      u32x4 o;
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x16 acc;
 #pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        uint32_t x[2][2];
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          // lanes 0-31 keep odd-group values and take the upper lanes' ones;
-          // lanes 32-63 take the lower lanes' even-group values
-          const auto r = __builtin_amdgcn_permlane32_swap(
-              __float_as_uint(acc[(2 * pr + 1) * 4 + e + u]),
-              __float_as_uint(acc[(2 * pr) * 4 + e + u]), false, false);
-          x[u][0] = r[0];
-          x[u][1] = r[1];
+      for (int k = 0; k < kSteps; ++k)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[nb][k]),
+                                                      xf[k], acc, 0, 0, 0);
+      // lane holds sequence b, dims n0 + 8 (i / 4) + 4 hf + i % 4
+      const int n0 = wave * 128 + nb * 32;
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          uint32_t x[2][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            // lanes 0-31 keep odd-group values and take the upper lanes' ones;
+            // lanes 32-63 take the lower lanes' even-group values
+            const auto rr2 = __builtin_amdgcn_permlane32_swap(
+                __float_as_uint(acc[(2 * pr + 1) * 4 + e + u]),
+                __float_as_uint(acc[(2 * pr) * 4 + e + u]), false, false);
+            x[u][0] = rr2[0];
+            x[u][1] = rr2[1];
+          }
+          o[e / 2] = pack_bf16x2(__uint_as_float(x[0][0]), __uint_as_float(x[1][0]));
+          o[2 + e / 2] = pack_bf16x2(__uint_as_float(x[0][1]), __uint_as_float(x[1][1]));
         }
-        o[e / 2] = pack_bf16x2(__uint_as_float(x[0][0]), __uint_as_float(x[1][0]));
-        o[2 + e / 2] = pack_bf16x2(__uint_as_float(x[0][1]), __uint_as_float(x[1][1]));
+        const int dim0 = n0 + 8 * (2 * pr + (hf ^ 1));
+        if (b < B) *(u32x4*)(q_abs + ((size_t)b * H + h) * kCache + dim0) = o;
       }
-      const int dim0 = n0 + 8 * (2 * pr + (hf ^ 1));
-      if (b < B) *(u32x4*)(q_abs + ((size_t)b * H + h) * kCache + dim0) = o;
-    }
-  }
-  if (blockIdx.x == 0) {
-    // 64 sequences x 64 rope values: 512 pieces of 16 bytes
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int piece = it * 256 + tid;
-      const int b = b0 + (piece >> 3), c = (piece & 7) * 8;
-      if (b < B)
-        *(u32x4*)(q_abs + ((size_t)b * H + h) * kCache + kLora + c) =
-            *(const u32x4*)(q + ((size_t)b * H + h) * kQDepth + kNope + c);
     }
   }
 }
@@ -943,7 +959,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
 // ---------------------------------------------------------------------------
 hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16_t* w_uk, int B,
                                 int H, const PrefixArgs& pa, hipStream_t stream) {
-  const dim3 grid(kLora / 128 + 1, H, (B + 63) / 64);
+  const dim3 grid(H + 1, (B + 63) / 64);
   hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), 0, stream, q_abs, q, w_uk, B, H, pa);
   return hipGetLastError();
 }
