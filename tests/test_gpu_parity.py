@@ -824,3 +824,36 @@ def test_decode_many_sequences_ragged_batch(B):
     _say("decode 130 sequences")
     for parts in (0, 300):
         _assert_close(_run_decode(B, wl, parts), oracle.decode(wl), BF16_MAX, BF16_MEAN)
+
+
+def test_unified_decode_at_full_size_matches_the_decode_entry(B):
+    # decode_b64 as the benchmark runs it through the graph op: each new
+    # token's raw row written, then the decode over cache_len + 1 rows; the
+    # dense decode entry over the written pool must agree bit for bit (its
+    # parity at this size is checked above), and sampled written rows must
+    # equal the oracle's normalised and rotated rows within one rounding
+    wl = decode_recipe("decode_b64")
+    ctx = wl.context_lens.astype(np.int64)
+    rng = np.random.default_rng(131)
+    x, gamma = _kv_raw(rng, len(ctx))
+    freqs = rope_table_bits(int(ctx.max()), 64)
+    t = decode_tensors(wl)
+    _say("unified decode, decode_b64")
+    out = B.prefill_decode(t["q"], _u32(np.arange(len(ctx) + 1)), _u32(ctx - 1), t["kv_cache"],
+                           t["page_table"], t["w_uk"], t["w_uv"], _dev_bf16(gamma),
+                           _dev_bf16(freqs), 1, int(ctx.max()) - 1, wl.scale, 1e-6,
+                           kv_input=_dev_bf16(x))
+    same = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
+                    t["w_uv"], int(ctx.max()), wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, same)
+    pool = t["kv_cache"]
+    for b in (0, 17, 63):
+        p = int(ctx[b]) - 1
+        slot = int(wl.page_table[b, p // wl.page_size]) * wl.page_size + p % wl.page_size
+        got = oracle.bf16_to_f64(bf16_bits(pool.reshape(-1, 576)[slot]))
+        latn, kr = oracle.norm_rope_rows(oracle.bf16_to_f64(x[b:b + 1]), [p],
+                                         oracle.bf16_to_f64(gamma), oracle.bf16_to_f64(freqs),
+                                         1e-6, 512)
+        ref = np.concatenate([latn[0], kr[0]])
+        assert (np.abs(got - ref) <= _stored_bound(ref, False)).all()
