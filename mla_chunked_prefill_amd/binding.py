@@ -395,27 +395,58 @@ def mla_prefill_decode(output, q, input_row_offsets, cache_lengths, kv_cache, pa
 # convenience: plan + workspace + call
 # ---------------------------------------------------------------------------
 
-def plan(input_row_offsets, cache_lengths, buffer_token_size: int, max_chunks: int,
-         stream=None):
-    """Run mla_prefill_plan into new device tensors; returns (bro, co, bl, chunks_needed)."""
-    B = cache_lengths.shape[0]
-    dev = cache_lengths.device
-    bro = torch.empty((max_chunks, B + 1), dtype=torch.uint32, device=dev)
-    co = torch.empty((max_chunks, B), dtype=torch.uint32, device=dev)
-    bl = torch.empty((max_chunks,), dtype=torch.int32, device=dev)
+def _plan_into(C, B, dev, input_row_offsets, cache_lengths, buffer_token_size, stream):
+    bro = torch.empty((C, B + 1), dtype=torch.uint32, device=dev)
+    co = torch.empty((C, B), dtype=torch.uint32, device=dev)
+    bl = torch.empty((C,), dtype=torch.int32, device=dev)
     need = torch.empty((1,), dtype=torch.uint32, device=dev)
     mla_prefill_plan(bro, co, bl, input_row_offsets, cache_lengths, buffer_token_size,
                      chunks_needed=need, stream=stream)
     return bro, co, bl, need
 
 
+def _read_chunks_needed(need, stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    s.synchronize()
+    return int(need.cpu()[0])
+
+
+def plan(input_row_offsets, cache_lengths, buffer_token_size: int,
+         max_chunks: int | None = None, stream=None):
+    """Run mla_prefill_plan into new device tensors; returns (bro, co, bl, chunks_needed).
+
+    A convenience path with one host read: the planner's chunks_needed is read
+    back once. max_chunks None plans exactly as many chunks as the batch needs
+    (at least one); a max_chunks below that raises ValueError, since the
+    queries of the chunks left out would never be attended. Callers that must
+    not synchronise (graph capture) call mla_prefill_plan directly."""
+    B = cache_lengths.shape[0]
+    dev = cache_lengths.device
+    C = 1 if max_chunks is None else int(max_chunks)
+    if C < 1:
+        raise ValueError(f"max_chunks must be >= 1, got {C}")
+    res = _plan_into(C, B, dev, input_row_offsets, cache_lengths, buffer_token_size, stream)
+    needed = _read_chunks_needed(res[3], stream)
+    if max_chunks is None:
+        if needed > C:
+            res = _plan_into(needed, B, dev, input_row_offsets, cache_lengths,
+                             buffer_token_size, stream)
+    elif needed > C:
+        raise ValueError(f"max_chunks={C} is below the {needed} chunks of "
+                         f"buffer_token_size={int(buffer_token_size)} this batch needs")
+    return res
+
+
 def prefill(q, input_row_offsets, cache_lengths, kv_cache, page_table, w_k, w_uv,
-            kv_norm_gamma, freqs_cis, buffer_token_size: int, max_chunks: int,
+            kv_norm_gamma, freqs_cis, buffer_token_size: int, max_chunks: int | None,
             max_prompt_len: int, scale: float, epsilon: float, max_rows: int | None = None,
             workspace=None, output=None, plan_tensors=None, stream=None, attn_sink=None):
     """Plan and run the whole chunked prefill; returns the bf16 output [Tq, H, 128].
 
-    max_rows defaults to batch_size * buffer_token_size (always enough)."""
+    max_rows defaults to batch_size * buffer_token_size (always enough). Without
+    plan_tensors the batch is planned here (plan(): one host read of the chunk
+    count; max_chunks None plans as many chunks as needed, a smaller
+    max_chunks raises)."""
     B = cache_lengths.shape[0]
     Tq, H = q.shape[0], q.shape[1]
     if max_rows is None:
@@ -475,12 +506,14 @@ def decode_sparse(q, topk_lengths, kv_cache, d_indices, w_uk, w_uv, max_topk: in
 def prefill_decode(q, input_row_offsets, cache_lengths, kv_cache, page_table, w_uk, w_uv,
                    kv_norm_gamma, freqs_cis, max_seq_len: int, max_cache_len: int,
                    scale: float, epsilon: float, kv_input=None, w_k=None,
-                   buffer_token_size: int = 8192, max_chunks: int = 1,
+                   buffer_token_size: int = 8192, max_chunks: int | None = None,
                    max_rows: int | None = None, d_indices=None, topk_lengths=None,
                    attn_sink=None, num_partitions: int = 0, workspace=None, output=None,
                    plan_tensors=None, stream=None):
-    """The graph op as one call (plans the chunks for a prefill); returns the
-    bf16 output [total_q, H, 128]."""
+    """The graph op as one call (plans the chunks for a prefill unless
+    plan_tensors are given: plan(), with one host read of the chunk count;
+    max_chunks None plans as many as needed, a smaller max_chunks raises);
+    returns the bf16 output [total_q, H, 128]."""
     B = cache_lengths.shape[0]
     Tq, H = q.shape[0], w_uv.shape[0]
     if max_seq_len > 1:

@@ -5,9 +5,9 @@ loop over Python floats (IEEE double), written independently of oracle.py so
 that the two tiers pin each other: on tiny inputs they must agree to rounding.
 
 The planner here walks tokens one at a time instead of using the closed form:
-position p of sequence b belongs to chunk p // T (mla_prefill_plan page,
-Args "buffer_token_size": each chunk processes at most this many tokens per
-sequence), and the plan arrays are read off that assignment.
+position p of sequence b belongs to chunk p // T, since T caps the tokens a
+sequence contributes to any one chunk (mla_prefill_plan page, Args
+"buffer_token_size"), and the plan arrays are read off that assignment.
 """
 from __future__ import annotations
 

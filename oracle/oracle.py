@@ -24,7 +24,7 @@ Sources, all Modular MAX kernel-library API pages:
 Readings where the pages leave a step open (each is listed in the design notes):
 - Chunks cap the tokens of each sequence: chunk c holds positions
   [c*T, min((c+1)*T, L_b)) of sequence b (mla_prefill_plan page, Args
-  "buffer_token_size": at most this many tokens per sequence).
+  "buffer_token_size", read as a per-sequence cap on a chunk's tokens).
 - cache_offsets of a sequence with no rows in a chunk is min(c*T, L_b); unused
   chunks are written in full with buffer_lengths = -1.
 - RoPE rotates adjacent pairs (2i, 2i+1) by the complex number whose real and

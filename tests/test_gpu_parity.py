@@ -228,12 +228,19 @@ def test_prefill_attention_given_kv(B):
 # end-to-end prefill
 # ---------------------------------------------------------------------------
 
-def _run_prefill(B, wl, max_rows=None):
+def _nan_out(*shape):
+    """An output tensor filled with NaN, so that a row no workgroup writes
+    fails the finiteness check."""
+    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+
+
+def _run_prefill(B, wl, max_rows=None, max_chunks=-1):
     t = prefill_tensors(wl)
     out = B.prefill(t["q"], t["input_row_offsets"], t["cache_lengths"], t["kv_cache"],
                     t["page_table"], t["w_k"], t["w_uv"], t["kv_norm_gamma"], t["freqs_cis"],
-                    wl.buffer_token_size, wl.max_chunks, int(wl.new_lens.max()), wl.scale,
-                    wl.eps, max_rows=max_rows)
+                    wl.buffer_token_size, wl.max_chunks if max_chunks == -1 else max_chunks,
+                    int(wl.new_lens.max()), wl.scale, wl.eps, max_rows=max_rows,
+                    output=_nan_out(wl.total_q, wl.num_heads, 128))
     torch.cuda.synchronize()
     return _f64(out)
 
@@ -266,43 +273,140 @@ def test_prefill_single_head_chunk_of_one(B):
     _assert_close(_run_prefill(B, wl), oracle.prefill(wl), BF16_MAX, BF16_MEAN)
 
 
-def _sample_pairs(wl, n, rng):
-    tq, H = wl.total_q, wl.num_heads
-    offs = wl.input_row_offsets
-    pairs = {(0, 0), (tq - 1, H - 1)}
+def _oracle_threads() -> int:
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _head_slice(wl, sel):
+    """The workload restricted to the heads in sel (their q, w_k, w_uv, w_uk)."""
+    d, H = wl.dims, wl.num_heads
+    w = dataclasses.replace(wl)
+    w.q = np.ascontiguousarray(wl.q[:, sel])
+    w.w_k = np.ascontiguousarray(wl.w_k.reshape(H, d.nope, d.lora)[sel].reshape(-1, d.lora))
+    w.w_uv = np.ascontiguousarray(wl.w_uv[sel])
+    w.w_uk = np.ascontiguousarray(wl.w_uk[sel])
+    w.num_heads = len(sel)
+    return w
+
+
+def _oracle_prefill_by_heads(wl, heads_per_slice=16):
+    """oracle.prefill over every head, run in head slices (one sequence's
+    materialised scores for all 128 heads would not fit in memory) on a
+    thread pool; BLAS is held to one thread inside the pool."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    H = wl.num_heads
+    slices = [list(range(h, min(h + heads_per_slice, H))) for h in range(0, H, heads_per_slice)]
+    out = np.empty((wl.total_q, H, wl.dims.v))
+    with threadpool_limits(1), cf.ThreadPoolExecutor(_oracle_threads()) as ex:
+        for sel, r in zip(slices, ex.map(lambda sl: oracle.prefill(_head_slice(wl, sl)), slices)):
+            out[:, sel[0]:sel[-1] + 1] = r
+    return out
+
+
+def _dense_samples(wl, rng):
+    """(t, h) rows for every head of every sequence: the sequence's first and
+    last query, one random query of each 128-query block, and the queries on
+    both sides of every chunk boundary (the first query whose keys span one
+    more chunk, and the one before it)."""
+    T = wl.buffer_token_size
+    offs = wl.input_row_offsets.astype(np.int64)
+    out = []
     for b in range(wl.batch):
-        if offs[b + 1] > offs[b]:
-            pairs.add((int(offs[b]), int(rng.integers(H))))
-            pairs.add((int(offs[b + 1]) - 1, int(rng.integers(H))))
-    while len(pairs) < n:
-        pairs.add((int(rng.integers(tq)), int(rng.integers(H))))
-    return sorted(pairs)
+        n, c = int(offs[b + 1] - offs[b]), int(wl.cached_lens[b])
+        if n == 0:
+            continue
+        qs = {0, n - 1}
+        for blk in range(0, n, 128):
+            qs.add(int(rng.integers(blk, min(blk + 128, n))))
+        k = (c // T + 1) * T  # first chunk boundary past the cached prefix
+        while k < c + n:
+            qs.update(i for i in (k - c - 1, k - c) if 0 <= i < n)
+            k += T
+        out += [(int(offs[b]) + i, h) for i in sorted(qs) for h in range(wl.num_heads)]
+    return out
 
 
-def _sampled_check(B, name, n, max_abs, mean_abs):
+def _oracle_prefill_sampled(wl, samples):
+    """oracle.prefill_sampled, one sequence per task of a thread pool."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    dec = oracle.Decoded(wl)
+    seq_of = np.searchsorted(wl.input_row_offsets[1:].astype(np.int64),
+                             [t for t, _ in samples], side="right")
+    groups: dict = {}
+    for i, b in enumerate(seq_of):
+        groups.setdefault(int(b), []).append(i)
+    res = np.empty((len(samples), wl.dims.v))
+
+    def run(b):
+        idx = groups[b]
+        return idx, oracle.prefill_sampled(wl, [samples[i] for i in idx], dec)
+
+    with threadpool_limits(1), cf.ThreadPoolExecutor(_oracle_threads()) as ex:
+        for idx, r in ex.map(run, sorted(groups)):
+            res[idx] = r
+    return res
+
+
+@pytest.mark.timeout(900)
+def test_prefill_dsv3_4k_full(B):
+    """Every output element of the 4096-token, 128-head prefill against the
+    oracle (run in 16-head slices): max-abs and mean-abs over all of them."""
+    wl = prefill_recipe("dsv3_prefill_4k")
+    _say("prefill dsv3_prefill_4k: running")
+    got = _run_prefill(B, wl)
+    _say("prefill dsv3_prefill_4k: oracle over all 128 heads")
+    ref = _oracle_prefill_by_heads(wl)
+    err = _assert_close(got, ref, BF16_MAX, BF16_MEAN)
+    _say(f"prefill dsv3_prefill_4k: {got.size} elements, max-abs {err.max():.3e}, "
+         f"mean-abs {err.mean():.3e}")
+
+
+def _dense_sampled_check(B, name, max_abs, mean_abs):
     _say(f"prefill {name}: generating")
     wl = prefill_recipe(name)
     _say(f"prefill {name}: running")
     got = _run_prefill(B, wl)
-    rng = np.random.default_rng(7)
-    pairs = _sample_pairs(wl, n, rng)
-    _say(f"prefill {name}: oracle on {len(pairs)} sampled rows")
-    ref = oracle.prefill_sampled(wl, pairs)
+    assert np.isfinite(got).all()  # every row written (outputs start as NaN)
+    pairs = _dense_samples(wl, np.random.default_rng(7))
+    _say(f"prefill {name}: oracle on {len(pairs)} sampled rows (every head of every sequence)")
+    ref = _oracle_prefill_sampled(wl, pairs)
     g = np.stack([got[t, h] for t, h in pairs])
-    assert np.isfinite(got).all()
-    _assert_close(g, ref, max_abs, mean_abs)
+    err = _assert_close(g, ref, max_abs, mean_abs)
+    _say(f"prefill {name}: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
 
 
-def test_prefill_dsv3_4k_sampled(B):
-    _sampled_check(B, "dsv3_prefill_4k", 48, BF16_MAX, BF16_MEAN)
+@pytest.mark.timeout(900)
+def test_prefill_ragged_b16_dense_sampled(B):
+    _dense_sampled_check(B, "ragged_b16_cached", BF16_MAX, BF16_MEAN)
 
 
-def test_prefill_ragged_b16_sampled(B):
-    _sampled_check(B, "ragged_b16_cached", 40, BF16_MAX, BF16_MEAN)
+@pytest.mark.timeout(900)
+def test_prefill_fp8_dense_sampled(B):
+    _dense_sampled_check(B, "fp8_ragged_b8_cached", FP8_MAX, None)
 
 
-def test_prefill_fp8_sampled(B):
-    _sampled_check(B, "fp8_ragged_b8_cached", 40, FP8_MAX, None)
+def test_prefill_max_chunks_derived_or_rejected(B):
+    """The convenience path reads the planner's chunk count: max_chunks None
+    plans every chunk the batch needs (tiny_b2 needs 3 chunks of 8 tokens),
+    and a max_chunks below that raises instead of leaving queries unwritten."""
+    wl = prefill_recipe("tiny_b2")
+    _assert_close(_run_prefill(B, wl, max_chunks=None), oracle.prefill(wl), BF16_MAX, BF16_MEAN)
+    with pytest.raises(ValueError, match="max_chunks"):
+        _run_prefill(B, wl, max_chunks=2)
+    t = prefill_tensors(wl)
+    with pytest.raises(ValueError, match="max_chunks"):
+        B.prefill_decode(t["q"], t["input_row_offsets"], t["cache_lengths"], t["kv_cache"],
+                         t["page_table"], t["w_uk"], t["w_uv"], t["kv_norm_gamma"],
+                         t["freqs_cis"], int(wl.new_lens.max()), int(wl.cached_lens.max()),
+                         wl.scale, wl.eps, w_k=t["w_k"], buffer_token_size=wl.buffer_token_size,
+                         max_chunks=1)
 
 
 def test_prefill_fp8_small_full(B):
@@ -318,7 +422,8 @@ def _run_decode(B, wl, num_partitions=0):
     t = decode_tensors(wl)
     out = B.decode(t["q"], t["context_lengths"], t["kv_cache"], t["page_table"], t["w_uk"],
                    t["w_uv"], int(wl.context_lens.max()), wl.scale,
-                   num_partitions=num_partitions)
+                   num_partitions=num_partitions,
+                   output=_nan_out(wl.batch, wl.num_heads, 128))
     torch.cuda.synchronize()
     return _f64(out)
 
@@ -334,16 +439,29 @@ def test_decode_all_heads_full(B):
     _assert_close(_run_decode(B, wl), oracle.decode(wl), BF16_MAX, BF16_MEAN)
 
 
-def test_decode_b64_sampled(B):
+def _oracle_decode_threaded(wl):
+    """oracle.decode over every sequence, one sequence per task of a thread pool."""
+    import concurrent.futures as cf
+
+    from threadpoolctl import threadpool_limits
+
+    dec = oracle.DecodedDecode(wl)
+    with threadpool_limits(1), cf.ThreadPoolExecutor(_oracle_threads()) as ex:
+        rows = list(ex.map(lambda b: oracle.decode(wl, dec, batch_indices=[b])[0],
+                           range(wl.batch)))
+    return np.stack(rows)
+
+
+@pytest.mark.timeout(900)
+def test_decode_b64_full(B):
+    """All 64 sequences (every key range of the split) against the oracle."""
     _say("decode_b64: generating")
     wl = decode_recipe("decode_b64")
     _say("decode_b64: running")
     got = _run_decode(B, wl)
-    idx = [0, 17, 40, 63]
-    _say("decode_b64: oracle on 4 sequences")
-    ref = oracle.decode(wl, batch_indices=idx)
-    assert np.isfinite(got).all()
-    _assert_close(got[idx], ref, BF16_MAX, BF16_MEAN)
+    _say("decode_b64: oracle on all 64 sequences")
+    err = _assert_close(got, _oracle_decode_threaded(wl), BF16_MAX, BF16_MEAN)
+    _say(f"decode_b64: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -414,16 +532,15 @@ def test_decode_fp8_single_key_widening_exact(B):
         assert np.all(np.abs(got[b] - ref[b]) <= bound), f"sequence {b}"
 
 
-def test_decode_b64_fp8_sampled(B):
+@pytest.mark.timeout(900)
+def test_decode_b64_fp8_full(B):
     _say("decode_b64_fp8: generating")
     wl = decode_recipe("decode_b64_fp8")
     _say("decode_b64_fp8: running")
     got = _run_decode(B, wl)
-    idx = [0, 31, 63]
-    _say("decode_b64_fp8: oracle on 3 sequences")
-    ref = oracle.decode(wl, batch_indices=idx)
-    assert np.isfinite(got).all()
-    _assert_close(got[idx], ref, FP8_MAX)
+    _say("decode_b64_fp8: oracle on all 64 sequences")
+    err = _assert_close(got, _oracle_decode_threaded(wl), FP8_MAX)
+    _say(f"decode_b64_fp8: max-abs {err.max():.3e}, mean-abs {err.mean():.3e}")
 
 
 # ---------------------------------------------------------------------------
