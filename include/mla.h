@@ -326,6 +326,36 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
                const float* attn_sink, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
 
+/*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation with the same kernels, its
+ * workspace taken from a scratch array built into the library instead of a
+ * caller buffer. The call allocates nothing; the caller still passes every
+ * input and the output.
+ *
+ * The scratch array holds MLA_NOALLOC_SCRATCH_BYTES (128 MiB); every GPU the
+ * library runs on holds its own copy until the process ends. A decode whose
+ * workspace (mla_decode_workspace_size with the same arguments) exceeds it
+ * is rejected with MLA_ERR_WORKSPACE before anything is enqueued; decode_b64's
+ * shape (64 sequences, 128 heads, contexts to 32k, one partition per compute
+ * unit) needs about 106 MiB. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give unspecified results. Nothing in
+ * the array has to start at zero; a call leaves its contents behind. The
+ * first call on a device looks up the array's device address (no
+ * allocation); make it outside graph capture.
+ * Arguments, limits and errors: as mla_decode, without workspace and
+ * workspace_bytes.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int mla_decode_noalloc(void* output, const void* q, const uint32_t* context_lengths,
+                       const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                       const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
+                       int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                       int32_t max_context_len, int32_t num_partitions, float scale,
+                       const float* attn_sink, hipStream_t stream);
+
 /* Text for a status code, and the message of the calling thread's last failure. */
 const char* mla_status_string(int status);
 const char* mla_last_error(void);

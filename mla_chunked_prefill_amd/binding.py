@@ -44,6 +44,8 @@ _SIGNATURES = {
     "mla_decode_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "mla_decode": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                         _P, _P, _S, _P]),
+    "mla_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                _F, _P, _P]),
     "mla_decode_sparse_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_decode_sparse": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F,
                                _P, _P, _S, _P]),
@@ -293,6 +295,24 @@ def mla_decode(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
         _sink_ptr(attn_sink, B), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("mla_decode", st)
+
+
+def mla_decode_noalloc(output, q, context_lengths, kv_cache, page_table, w_uk, w_uv,
+                       max_context_len: int, scale: float, num_partitions: int = 0,
+                       stream=None, attn_sink=None):
+    """mla_decode with its workspace in the library's fixed scratch array."""
+    B, H = q.shape[0], q.shape[1]
+    _expect(output, torch.bfloat16, (B, H, VD), "output")
+    _expect(q, torch.bfloat16, (B, H, QD), "q")
+    _expect(context_lengths, torch.uint32, (B,), "context_lengths")
+    _expect(w_uk, torch.bfloat16, (H, LORA, NOPE), "w_uk")
+    _expect(w_uv, torch.bfloat16, (H, VD, LORA), "w_uv")
+    st = load().mla_decode_noalloc(
+        _ptr(output), _ptr(q), _ptr(context_lengths), _ptr(kv_cache), _dtype_code(kv_cache),
+        _ptr(page_table), _ptr(w_uk), _ptr(w_uv), B, H, kv_cache.shape[1], page_table.shape[1],
+        kv_cache.shape[0], int(max_context_len), int(num_partitions), float(scale),
+        _sink_ptr(attn_sink, B), _stream(stream))
+    _check("mla_decode_noalloc", st)
 
 
 def mla_decode_sparse_workspace_size(batch_size: int, num_heads: int, max_topk: int,

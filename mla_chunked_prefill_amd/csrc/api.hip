@@ -2,6 +2,7 @@
 // launches. Declarations and contracts are in include/mla.h.
 #include <initializer_list>
 #include <math.h>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -522,6 +523,73 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
   return decode_body(output, q, context_lengths, 0, kv_cache, cache_dtype, page_table, w_uk,
                      w_uv, batch_size, num_heads, page_size, max_pages_per_seq, num_pages,
                      max_context_len, num_partitions, scale, attn_sink, workspace, stream);
+}
+
+// Allocation-free decode: the workspace of mla_decode lives in this array, one
+// copy per GPU (each device that loads the library holds it until the process
+// ends). Host code never passes the array's name to a kernel: its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and is kept per device.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "mla_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc: device %d beyond %d", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "mla_decode_noalloc: hipGetSymbolAddress of the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+}  // namespace
+
+int mla_decode_noalloc(void* output, const void* q, const uint32_t* context_lengths,
+                       const void* kv_cache, int32_t cache_dtype, const int32_t* page_table,
+                       const void* w_uk, const void* w_uv, int32_t batch_size, int32_t num_heads,
+                       int32_t page_size, int32_t max_pages_per_seq, int32_t num_pages,
+                       int32_t max_context_len, int32_t num_partitions, float scale,
+                       const float* attn_sink, hipStream_t stream) {
+  if (!output || !q || !context_lengths || !kv_cache || !page_table || !w_uk || !w_uv)
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc: null pointer");
+  if (misaligned({output, q, kv_cache, w_uk, w_uv}))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc: tensor not 16-byte aligned");
+  if (!dtype_ok(cache_dtype)) return fail(MLA_ERR_UNSUPPORTED, "mla_decode_noalloc: dtype");
+  if (batch_size < 1 || num_heads < 1 || num_heads > 128 || page_size < 1 ||
+      max_pages_per_seq < 1 || num_pages < 1 || max_context_len < 1 || num_partitions < 0 ||
+      num_partitions > 65536 || !(scale > 0.f))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc: sizes (num_heads must be 1..128)");
+  if ((uint64_t)batch_size * (uint64_t)max_context_len >= (1ull << 31) ||
+      (uint64_t)num_pages * (uint64_t)page_size >= (1ull << 31))
+    return fail(MLA_ERR_INVALID_ARG, "mla_decode_noalloc: batch_size * max_context_len and "
+                "num_pages * page_size must be < 2^31");
+  const size_t need = mla_decode_workspace_size(batch_size, num_heads, max_context_len,
+                                                page_size, num_partitions, cache_dtype);
+  if (need == 0 || need > (size_t)MLA_NOALLOC_SCRATCH_BYTES)
+    return fail(MLA_ERR_WORKSPACE,
+                "mla_decode_noalloc: this decode needs %zu bytes of scratch, beyond the "
+                "library's fixed %zu (use mla_decode with a workspace)",
+                need, (size_t)MLA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  return decode_body(output, q, context_lengths, 0, kv_cache, cache_dtype, page_table, w_uk,
+                     w_uv, batch_size, num_heads, page_size, max_pages_per_seq, num_pages,
+                     max_context_len, num_partitions, scale, attn_sink, ws, stream);
 }
 
 // The absorbed decode (arguments already checked): context length of sequence

@@ -85,6 +85,21 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
                           0, 0.1, None, fake, 1 << 40, None) == -1
 
 
+def test_noalloc_decode_rejects_before_any_launch(lib):
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, fake, fake, fake, 0, fake, fake, fake, 64, 128, 64, 512, 10000, 32768]
+    # null input
+    assert lib.mla_decode_noalloc(fake, None, *args[2:], 0, 0.1, None, None) == -1
+    # a decode whose workspace exceeds the fixed scratch array (128 MiB): the
+    # size check comes before the device is touched
+    need = lib.mla_decode_workspace_size(64, 128, 32768, 64, 65536, 0)
+    assert need > (128 << 20)
+    assert lib.mla_decode_noalloc(*args, 65536, 0.1, None, None) == -3
+    assert b"scratch" in lib.mla_last_error()
+    # the default partition count of a 64 x 32k, 128-head decode fits
+    assert lib.mla_decode_workspace_size(64, 128, 32768, 64, 0, 0) <= (128 << 20)
+
+
 def test_workspace_sizes_grow_with_problem(lib):
     a = lib.mla_prefill_workspace_size(2, 100, 4, 256, 0)
     b = lib.mla_prefill_workspace_size(2, 100, 4, 512, 0)
