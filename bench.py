@@ -1,33 +1,42 @@
 """Benchmark: MLA chunked prefill (and absorbed decode) on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S] [--no-decode] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S]
+                [--phases prefill,ragged,decode,sparse,kvwrite,unified,hbm,cpu]
+                [--no-decode] [--no-cpu]
 
 A step is one pass of the prefill path over the DeepSeek-V3-shaped batch (one
 4096-token prompt, no cache, 128 heads): mla_prefill_plan, then for every chunk
 slot mla_gather_norm_rope, mla_up_project and mla_prefill_attention, all
 through the C ABI on torch's current stream. Inputs are resident in HBM before
 the timed region. HIP events recorded on that stream around every call give
-per-call durations; the attention call is the dominant kernel.
+per-call durations; the attention call is the dominant kernel. "value" is the
+end-to-end prefill rate in algorithmic attention TFLOP/s (attention FLOPs /
+whole step time); "roofline" is the attention call alone against the bf16
+dense MFMA peak, with HBM traffic and MFMA-busy figures from committed counter
+summaries taken on the same kernel source (else null).
 
-A second phase times K calls of mla_decode on the 64-sequence absorbed-decode
-batch (contexts U{4096..32768}), with a bf16 and then an e4m3 cache, and
-reports achieved HBM bandwidth, then mla_decode_sparse with every sequence
-listing 2048 rows of its context. Then mla_kv_write stores the prompt's 4096
-new tokens into the paged cache (normalised, rotated; timed as HIP graph
-replays, the launches being shorter than the host's issue time), and
-mla_prefill_decode runs the graph op as one call in its prefill branch (write
-+ prefill over stored rows) and its decode branch (write + decode, also as
-graph replays).
+Further phases, each reported under its own key:
+- ragged: the two ragged batches with cached prefixes and three chunks
+  (ragged_b16_cached in bf16, fp8_ragged_b8_cached with q and the pool in
+  e4m3): per chunk gather (timed after a cache flush), up-projection and
+  attention in pipeline order, and the whole mla_prefill call; attention
+  against the bf16 peak, or the fp8 peak and the mixed fp8/bf16 roofline.
+- decode: mla_decode on the 64-sequence absorbed-decode batch (contexts
+  U{4096..32768}) with a bf16 and an e4m3 cache, in HBM GB/s.
+- sparse: mla_decode_sparse with every sequence listing 2048 rows.
+- kvwrite: mla_kv_write of the prompt's 4096 new tokens.
+- unified: mla_prefill_decode in its prefill and decode branches.
+- hbm: the practical HBM rates of torch's own read and copy kernels.
+- cpu: the fp64 oracle timed on bounded samples of every workload (and the
+  scalar tier on the tiny one), on this host's cores.
+Every timed rep of an HBM-bound call (decode, sparse decode, KV write,
+gather) is preceded by reading a 1 GiB buffer, so that neither L2 nor the
+256 MiB MALL still holds its inputs (the decode is also timed after writing
+the buffer, and back to back without a flush).
 
 Before the W warm-up steps, about S seconds (default 1) of the same work run
 untimed, so that the GPU clock has left its idle state; the K timed steps are
-exactly K.
-
-One JSON line is printed. "value" is the end-to-end prefill rate in
-algorithmic attention TFLOP/s (attention FLOPs / whole step time);
-"roofline" is the attention call alone against the bf16 dense MFMA peak.
-"cpu_baseline" times the fp64 CPU oracle on a bounded sample of the same
-prefill workload (a few of its heads).
+exactly K. One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -106,6 +115,82 @@ def graph_ms(fn, per_graph: int, reps: int, torch):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (reps * per_graph)
+
+
+class Flusher:
+    """Evicts the caches before a timed rep of an HBM-bound call: reads a 1 GiB
+    device buffer (written once here), so that neither L2 nor the 256 MiB MALL
+    still holds the call's inputs. Reading leaves clean lines behind; a flush
+    that writes the buffer leaves dirty lines whose write-back lands inside
+    the timed call (mode "write", kept for comparison)."""
+
+    def __init__(self, torch, mode: str = "read"):
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+        self.mode = mode
+        self.k = 0
+
+    def __call__(self):
+        if self.mode == "read":
+            self.buf.sum()
+        elif self.mode == "write":
+            self.k = (self.k + 1) & 0x7F
+            self.buf.fill_(float(self.k))
+
+
+def flushed_ms(fn, steps: int, flush, torch):
+    """Per-call durations (ms) of fn between two events, each call preceded by
+    a cache flush outside the events; returns (mean, median, min)."""
+    evs = []
+    for _ in range(steps):
+        flush()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2], ms[0]
+
+
+def hbm_ceiling(binding, torch, reps: int = 10):
+    """Practical HBM rates: the library's plain streaming-read kernel over
+    4 GiB (best of a few grid sizes), torch's sum over the same 4 GiB (reads
+    only) and a 2 GiB torch device copy (reads + writes)."""
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    probe = {}
+    for groups in (1024, 2048, 4096, 8192):
+        out = torch.empty(groups, dtype=torch.uint32, device="cuda")
+        probe[groups] = rate(lambda: binding.mla_hbm_read(x, out, groups), 4 << 30)
+    best = max(probe, key=probe.get)
+    tsum = rate(lambda: x.sum(), 4 << 30)
+    del x
+    src = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy = rate(lambda: dst.copy_(src), 4 << 30)
+    del src, dst
+    return dict(read_gbps=round(probe[best], 1), read_groups=best,
+                read_gbps_by_groups={str(k): round(v, 1) for k, v in probe.items()},
+                torch_sum_read_gbps=round(tsum, 1), torch_copy_gbps=round(copy, 1),
+                how="mla_hbm_read (16-byte streaming loads, 256-thread workgroups) over 4 GiB; "
+                    "torch.sum over the same 4 GiB; 2 GiB torch device copy counted as "
+                    "read + write")
 
 
 def event_ms(fn, steps: int, torch):
@@ -200,7 +285,144 @@ def bench_prefill(args, binding, torch):
         attn_flop=attn_flop, gemm_flop=gemm_flop, pairs=pairs, max_rows=max_rows)
 
 
-def bench_decode(args, binding, torch, recipe="decode_b64", sinks=False):
+PEAK_FP8_TFLOPS = 5000.0
+
+
+def chunk_pairs(bro, co, new_lens, cached_lens, c: int) -> int:
+    """Visible (query, key) pairs whose key lies in chunk c: query i of
+    sequence b sits at position cached + i and sees the chunk's keys at
+    positions co .. co + rows - 1 that are not after it."""
+    import numpy as np
+
+    tot = 0
+    for b in range(len(new_lens)):
+        rows = int(bro[c, b + 1]) - int(bro[c, b])
+        n, cb, k0 = int(new_lens[b]), int(cached_lens[b]), int(co[c, b])
+        if rows == 0 or n == 0:
+            continue
+        P = cb + np.arange(n, dtype=np.int64)
+        tot += int(np.clip(P - k0 + 1, 0, rows).sum())
+    return tot
+
+
+def bench_prefill_ragged(args, binding, torch, flush, name):
+    """A ragged batch with cached prefixes over several chunks (all 128 heads):
+    per-call times of every chunk's gather (after a cache flush), up-projection
+    and attention, run in pipeline order, and of the whole mla_prefill call."""
+    import numpy as np
+    from workloads import prefill_recipe
+    from workloads.device import prefill_tensors
+
+    wl = prefill_recipe(name)
+    t = prefill_tensors(wl)
+    B, H, T, C, Tq = wl.batch, wl.num_heads, wl.buffer_token_size, wl.max_chunks, wl.total_q
+    fp8 = bool(wl.fp8)
+    kdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    max_rows = (int(min(B * T, sum(min(int(L), T) for L in wl.seq_lens))) + 63) // 64 * 64
+    bro, co, bl, _ = binding.plan(t["input_row_offsets"], t["cache_lengths"], T, C)
+    bro_h, co_h, bl_h = bro.cpu().numpy(), co.cpu().numpy(), bl.cpu().numpy()
+    chunks = [c for c in range(C) if bl_h[c] > 0]
+    dev = "cuda"
+    latn = torch.empty((max_rows, 512), dtype=torch.bfloat16, device=dev)
+    krope = torch.empty((max_rows, 64), dtype=kdt, device=dev)
+    k_nope = torch.empty((H, max_rows, 128), dtype=kdt, device=dev)
+    v_t = torch.empty((H, 128, max_rows), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((Tq, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(binding.mla_prefill_attention_workspace_size(B, Tq, H), dtype=torch.uint8,
+                     device=dev)
+    max_prompt = int(wl.new_lens.max())
+    bro_c = [bro[c].contiguous() for c in range(C)]
+    co_c = [co[c].contiguous() for c in range(C)]
+
+    def gather(c):
+        binding.mla_gather_norm_rope(latn, krope, t["kv_cache"], t["page_table"], bro_c[c],
+                                     co_c[c], bl[c:c + 1], t["kv_norm_gamma"], t["freqs_cis"],
+                                     wl.eps)
+
+    def up(c):
+        binding.mla_up_project(k_nope, v_t, latn, t["w_k"], t["w_uv"], bl[c:c + 1])
+
+    def attn(c):
+        binding.mla_prefill_attention(out, t["q"], k_nope, v_t, krope, t["input_row_offsets"],
+                                      t["cache_lengths"], bro_c[c], co_c[c], bl[c:c + 1],
+                                      max_prompt, wl.scale, ws)
+
+    def pipeline(ev):
+        for c in chunks:
+            for nm, fn in (("gather", gather), ("up_project", up), ("attention", attn)):
+                if ev is None:
+                    fn(c)
+                    continue
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(c)
+                e1.record()
+                ev.setdefault((nm, c), []).append((e0, e1))
+
+    warm_clock(lambda: pipeline(None), args.warm_seconds / 2, torch)
+    for _ in range(args.warmup):
+        pipeline(None)
+    torch.cuda.synchronize()
+    ev = {}
+    for _ in range(args.steps):
+        pipeline(ev)
+    torch.cuda.synchronize()
+    ms = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in ev.items()}
+    # the gather alone after a cache flush (HBM-bound)
+    gather_ms = {c: flushed_ms(lambda: gather(c), args.steps, flush, torch)[0] for c in chunks}
+    # the whole call (plan given)
+    pws = torch.empty(binding.mla_prefill_workspace_size(B, Tq, H, max_rows,
+                                                         binding.MLA_FP8_E4M3FN if fp8
+                                                         else binding.MLA_BF16),
+                      dtype=torch.uint8, device=dev)
+
+    def full():
+        binding.mla_prefill(out, t["q"], t["input_row_offsets"], t["cache_lengths"],
+                            t["kv_cache"], t["page_table"], bro, co, bl, max_rows, t["w_k"],
+                            t["w_uv"], t["kv_norm_gamma"], t["freqs_cis"], max_prompt, wl.scale,
+                            wl.eps, pws)
+
+    for _ in range(args.warmup):
+        full()
+    full_ms = event_ms(full, args.steps, torch)
+    pairs = {c: chunk_pairs(bro_h, co_h, wl.new_lens, wl.cached_lens, c) for c in chunks}
+    tot_pairs = sum(pairs.values())
+    assert tot_pairs == visible_pairs(wl.new_lens, wl.cached_lens)
+    f_qk, f_pv = 2 * 192 * H * tot_pairs, 2 * 128 * H * tot_pairs
+    attn_ms = sum(ms[("attention", c)] for c in chunks)
+    attn_tf = (f_qk + f_pv) / (attn_ms * 1e-3) / 1e12
+    rows = {c: int(bl_h[c]) for c in chunks}
+    row_bytes = (576 if fp8 else 1152) + 128 + 1024 + (64 if fp8 else 128)
+    g_bytes = sum(rows[c] * row_bytes for c in chunks)
+    g_ms = sum(gather_ms.values())
+    up_flop = sum(2 * rows[c] * 512 * 2 * H * 128 for c in chunks)
+    up_ms = sum(ms[("up_project", c)] for c in chunks)
+    res = dict(
+        batch=B, total_q=Tq, chunks=len(chunks), rows_per_chunk=[rows[c] for c in chunks],
+        visible_pairs=tot_pairs, attn_flop=f_qk + f_pv,
+        mla_prefill_ms=round(full_ms, 4),
+        mla_prefill_attn_tflops=round((f_qk + f_pv) / (full_ms * 1e-3) / 1e12, 2),
+        attention_ms_per_chunk=[round(ms[("attention", c)], 4) for c in chunks],
+        attention_ms=round(attn_ms, 4), attention_tflops=round(attn_tf, 2),
+        up_project_ms=round(up_ms, 4),
+        up_project_tflops=round(up_flop / (up_ms * 1e-3) / 1e12, 2),
+        gather_ms_per_chunk_flushed=[round(gather_ms[c], 4) for c in chunks],
+        gather_bytes=g_bytes, gather_gbps=round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+        gather_frac_hbm=round(g_bytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+    if fp8:
+        # scores on fp8 MFMA, the value product on bf16 MFMA
+        t_mixed = f_qk / (PEAK_FP8_TFLOPS * 1e12) + f_pv / (PEAK_BF16_TFLOPS * 1e12)
+        res.update(attention_frac_fp8_peak=round(attn_tf / PEAK_FP8_TFLOPS, 4),
+                   attention_frac_mixed_roofline=round(t_mixed / (attn_ms * 1e-3), 4),
+                   mixed_roofline="t = F_QK / 5.0 PFLOP/s (fp8) + F_PV / 2.5 PFLOP/s (bf16)")
+    else:
+        res.update(attention_frac_bf16_peak=round(attn_tf / PEAK_BF16_TFLOPS, 4))
+    del t, latn, krope, k_nope, v_t, out, ws, pws
+    return wl, res
+
+
+def bench_decode(args, binding, torch, flush, recipe="decode_b64", sinks=False):
     from workloads import decode_recipe
     from workloads.device import decode_tensors
 
@@ -223,24 +445,16 @@ def bench_decode(args, binding, torch, recipe="decode_b64", sinks=False):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    evs = []
-    for _ in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ms, med, mn = flushed_ms(call, args.steps, flush, torch)
     ctx_rows = int(wl.context_lens.astype("int64").sum())
     row_bytes = 576 * (1 if wl.fp8 else 2)
     bytes_alg = (ctx_rows * row_bytes + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2)
     flop = 2 * (576 + 512) * H * ctx_rows
-    return dict(ms=ms, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows)
+    return dict(ms=ms, median_ms=med, min_ms=mn, bytes=bytes_alg, flop=flop, ctx_rows=ctx_rows,
+                wl=wl)
 
 
-def bench_decode_sparse(args, binding, torch, topk=2048):
+def bench_decode_sparse(args, binding, torch, flush, topk=2048):
     """mla_decode_sparse on decode_b64's pool, queries and weights: every
     sequence lists `topk` distinct rows of its own context (uniform positions,
     sorted, mapped through its page table)."""
@@ -272,28 +486,19 @@ def bench_decode_sparse(args, binding, torch, topk=2048):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    evs = []
-    for _ in range(args.steps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    ms, med, mn = flushed_ms(call, args.steps, flush, torch)
     nrows = B * topk
     bytes_alg = nrows * 576 * 2 + 2 * H * 512 * 128 * 2 + B * H * 192 * 2 + B * H * 128 * 2 + nrows * 4
     flop = 2 * (576 + 512) * H * nrows
-    return dict(ms=ms, bytes=bytes_alg, flop=flop)
+    return dict(ms=ms, median_ms=med, min_ms=mn, bytes=bytes_alg, flop=flop)
 
 
-def bench_kv_write(args, binding, torch):
+def bench_kv_write(args, binding, torch, flush):
     """mla_kv_write on the prompt of dsv3_prefill_4k: 4096 new tokens' raw
     576-wide rows normalised, rotated and stored in a bf16 pool of 128-row
-    pages (shuffled page table). A launch takes microseconds, less than the
-    host needs to issue it, so 20 calls are captured into a HIP graph whose
-    replays are timed."""
+    pages (shuffled page table). Timed per call after a cache flush (the
+    flush keeps the GPU busy while the host issues the call), and as replays
+    of a HIP graph of 20 back-to-back calls over the same, cached, buffers."""
     import numpy as np
     from workloads import f32_to_bf16_bits
     from workloads.gen import rope_table_bits
@@ -316,9 +521,10 @@ def bench_kv_write(args, binding, torch):
         binding.mla_kv_write(cache, pt, x, offs, clen, gamma, freqs, 1e-6)
 
     warm_clock(call, args.warm_seconds / 4, torch)
-    ms = graph_ms(call, 20, max(1, args.steps // 2), torch)
+    ms, med, mn = flushed_ms(call, args.steps, flush, torch)
+    gms = graph_ms(call, 20, max(1, args.steps // 2), torch)
     bytes_alg = n * (576 * 2 + 576 * 2 + 64 * 2) + 512 * 2
-    return dict(ms=ms, bytes=bytes_alg)
+    return dict(ms=ms, median_ms=med, min_ms=mn, graph_ms=gms, bytes=bytes_alg)
 
 
 def bench_unified(args, binding, torch):
@@ -399,36 +605,114 @@ def bench_unified(args, binding, torch):
     return res
 
 
-def cpu_baseline(full_wl, heads: int):
-    """The oracle as it stands on `heads` of the 128 heads of the same prefill
-    workload; returns (attention TFLOP/s on the sample, seconds, threads)."""
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def _head_slice(wl, sel):
+    """The prefill workload restricted to the heads in sel (their q, w_k,
+    w_uv and w_uk slices)."""
     import dataclasses
 
     import numpy as np
 
+    d, H = wl.dims, wl.num_heads
+    w = dataclasses.replace(wl)
+    w.q = np.ascontiguousarray(wl.q[:, sel])
+    w.w_k = np.ascontiguousarray(wl.w_k.reshape(H, d.nope, d.lora)[sel].reshape(-1, d.lora))
+    w.w_uv = np.ascontiguousarray(wl.w_uv[sel])
+    w.w_uk = np.ascontiguousarray(wl.w_uk[sel])
+    w.num_heads = len(sel)
+    return w
+
+
+def cpu_baseline(full_wl, heads: int):
+    """The oracle as it stands on `heads` of the 128 heads of the same prefill
+    workload; returns (attention TFLOP/s on the sample, seconds, threads)."""
+    import numpy as np
+
     from oracle import oracle
 
-    wl = dataclasses.replace(full_wl)
-    d = wl.dims
-    H = wl.num_heads
-    sel = list(range(heads))
-    # restrict the workload to the sampled heads (their q, w_k and w_uv slices)
-    wl.q = wl.q[:, sel]
-    wl.w_k = wl.w_k.reshape(H, d.nope, d.lora)[sel].reshape(-1, d.lora)
-    wl.w_uv = wl.w_uv[sel]
-    wl.w_uk = wl.w_uk[sel]
-    wl.num_heads = heads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    wl = _head_slice(full_wl, list(range(heads)))
+    threads = _blas_threads()
     t0 = time.perf_counter()
     out = oracle.prefill(wl)
     sec = time.perf_counter() - t0
     assert np.isfinite(out).all()
     flop = 2 * (192 + 128) * heads * visible_pairs(wl.new_lens, wl.cached_lens)
     return flop / sec / 1e12, sec, threads
+
+
+def oracle_timings(ragged, dec_wl):
+    """The oracle (and, on the tiny batch, the scalar tier) timed on bounded
+    samples of the other workloads; rates in algorithmic FLOPs of the sample."""
+    import numpy as np
+
+    from oracle import brute, oracle
+    from workloads import prefill_recipe
+
+    res = {}
+    wl0 = prefill_recipe("tiny_b2")
+    f0 = 2 * (192 + 128) * wl0.num_heads * visible_pairs(wl0.new_lens, wl0.cached_lens)
+    t0 = time.perf_counter()
+    oracle.prefill(wl0)
+    s0 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    brute.prefill(wl0)
+    sb = time.perf_counter() - t0
+    res["tiny_b2"] = dict(sample="whole workload", oracle_seconds=round(s0, 4),
+                          oracle_gflops=round(f0 / s0 / 1e9, 3),
+                          brute_seconds=round(sb, 3), brute_gflops=round(f0 / sb / 1e9, 5),
+                          brute_cores=1)
+    for name, wl in ragged.items():
+        w = _head_slice(wl, [0])
+        f = 2 * (192 + 128) * visible_pairs(w.new_lens, w.cached_lens)
+        t0 = time.perf_counter()
+        out = oracle.prefill(w)
+        sec = time.perf_counter() - t0
+        assert np.isfinite(out).all()
+        res[name] = dict(sample="whole prefill (gather, RMSNorm, RoPE, up-projection, "
+                                "attention) of every sequence, head 0 of 128",
+                         oracle_seconds=round(sec, 2), oracle_gflops=round(f / sec / 1e9, 3))
+    idx = list(range(8))
+    f = 2 * (576 + 512) * dec_wl.num_heads * int(dec_wl.context_lens[idx].astype(np.int64).sum())
+    t0 = time.perf_counter()
+    oracle.decode(dec_wl, batch_indices=idx)
+    sec = time.perf_counter() - t0
+    res[dec_wl.name] = dict(sample="absorbed decode of sequences 0..7 of 64, all 128 heads",
+                            oracle_seconds=round(sec, 2), oracle_gflops=round(f / sec / 1e9, 3))
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def load_counters(name: str, kernel_file: str):
+    """A committed counter summary, if it was taken on the current source of
+    its kernel; else None."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash(kernel_file):
+        return None
+    return d
+
+
+PHASES = ("prefill", "ragged", "decode", "sparse", "kvwrite", "unified", "hbm", "cpu")
 
 
 def main():
@@ -438,8 +722,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--warm-seconds", type=float, default=1.0,
                     help="untimed run of the same work before the warm-up steps")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--phases", default=",".join(PHASES),
+                    help="comma-separated subset of " + ",".join(PHASES) +
+                         " (prefill, the headline, always runs)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode, sparse and unified phases")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timings")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter calibration)")
@@ -448,6 +736,11 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    phases = set(x.strip() for x in args.phases.split(",") if x.strip())
+    if args.no_decode:
+        phases -= {"decode", "sparse", "unified"}
+    if args.no_cpu:
+        phases.discard("cpu")
 
     import torch
 
@@ -461,10 +754,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    flush = Flusher(torch)
     p = bench_prefill(args, binding, torch)
     attn_tflops = p["attn_flop"] / (p["attn_ms"] * 1e-3) / 1e12
     value = p["attn_flop"] / (p["wall_ms"] * 1e-3) / 1e12
     traffic = load_traffic("attn.hip", "attn_dsv3_prefill_4k_counters.json")
+    mfma = load_counters("attn_dsv3_prefill_4k_counters.json", "attn.hip")
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -492,30 +787,48 @@ def main():
             "traffic": traffic,
             "algorithmic_flop_per_launch": p["attn_flop"],
             "avg_launch_ms": round(p["attn_ms"], 4),
+            "mfma_busy": None if mfma is None else mfma.get("mfma_busy"),
+            "valu_per_mfma": None if mfma is None else mfma.get("valu_per_mfma"),
         },
         "prefill_breakdown_ms": {k: round(v, 4) for k, v in p["per_call_ms"].items()},
         "prefill_end_to_end_tflops": round((p["attn_flop"] + p["gemm_flop"]) /
                                            (p["wall_ms"] * 1e-3) / 1e12, 2),
     }
-    if not args.no_decode:
-        dd = bench_decode(args, binding, torch)
+    ragged = {}
+    if "ragged" in phases:
+        for key, name in (("prefill_ragged_b16", "ragged_b16_cached"),
+                          ("prefill_fp8_ragged_b8", "fp8_ragged_b8_cached")):
+            wl, r = bench_prefill_ragged(args, binding, torch, flush, name)
+            r["workload"] = (f"{name}: {wl.batch} prompts, new U{{128..4096}}, cached "
+                             f"U{{0..8192}}, 128 heads, page 128, buffer_token_size 8192"
+                             + (", q and pool float8_e4m3fn" if wl.fp8 else ", bf16"))
+            line[key] = r
+            ragged[name] = wl
+            torch.cuda.empty_cache()
+    dec_wl = None
+    if "decode" in phases:
+        dd = bench_decode(args, binding, torch, flush)
+        dec_wl = dd["wl"]
         gbps = dd["bytes"] / (dd["ms"] * 1e-3) / 1e9
         line["decode"] = {
             "workload": "decode_b64: 64 sequences, one new token each, contexts "
                         "U{4096..32768}, 128 heads, 576-wide bf16 latent cache, page 64",
-            "ms": round(dd["ms"], 4),
+            "ms": round(dd["ms"], 4), "median_ms": round(dd["median_ms"], 4),
+            "min_ms": round(dd["min_ms"], 4),
             "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes": dd["bytes"],
             "tflops": round(dd["flop"] / (dd["ms"] * 1e-3) / 1e12, 2),
+            "timing": "each call after reading a 1 GiB buffer (cache flush)",
             "split_kernel_traffic": load_traffic("decode.hip", "decode_split_decode_b64_counters.json"),
         }
-        d8 = bench_decode(args, binding, torch, "decode_b64_fp8")
+        d8 = bench_decode(args, binding, torch, flush, "decode_b64_fp8")
         gbps = d8["bytes"] / (d8["ms"] * 1e-3) / 1e9
         line["decode_fp8"] = {
             "workload": "decode_b64_fp8: as decode_b64 with the cache stored float8_e4m3fn "
                         "(unit amax)",
-            "ms": round(d8["ms"], 4),
+            "ms": round(d8["ms"], 4), "median_ms": round(d8["median_ms"], 4),
+            "min_ms": round(d8["min_ms"], 4),
             "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes": d8["bytes"],
@@ -523,30 +836,42 @@ def main():
             "split_kernel_traffic": load_traffic("decode.hip",
                                                  "decode_split_decode_b64_fp8_counters.json"),
         }
-        dk = bench_decode(args, binding, torch, sinks=True)
+        dk = bench_decode(args, binding, torch, flush, sinks=True)
         line["decode"]["ms_with_sinks"] = round(dk["ms"], 4)
-        ds = bench_decode_sparse(args, binding, torch)
+        flush.mode = "write"
+        dw = bench_decode(args, binding, torch, flush)
+        flush.mode = "none"
+        dn = bench_decode(args, binding, torch, flush)
+        flush.mode = "read"
+        line["decode"]["ms_after_write_flush"] = round(dw["ms"], 4)
+        line["decode"]["ms_back_to_back_no_flush"] = round(dn["ms"], 4)
+    if "sparse" in phases:
+        ds = bench_decode_sparse(args, binding, torch, flush)
         gbps = ds["bytes"] / (ds["ms"] * 1e-3) / 1e9
         line["decode_sparse"] = {
             "workload": "mla_decode_sparse: decode_b64's 64 sequences, each attending over "
                         "2048 distinct rows of its own context listed by physical index",
-            "ms": round(ds["ms"], 4),
+            "ms": round(ds["ms"], 4), "median_ms": round(ds["median_ms"], 4),
             "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(gbps / PEAK_HBM_GBPS, 4),
             "algorithmic_bytes": ds["bytes"],
             "tflops": round(ds["flop"] / (ds["ms"] * 1e-3) / 1e12, 2),
+            "timing": "each call after reading a 1 GiB buffer (cache flush)",
         }
-    kw = bench_kv_write(args, binding, torch)
-    gbps = kw["bytes"] / (kw["ms"] * 1e-3) / 1e9
-    line["kv_write"] = {
-        "workload": "mla_kv_write: the 4096 new tokens of dsv3_prefill_4k, raw 576-wide rows "
-                    "normalised, rotated and stored into a bf16 pool of 128-row pages",
-        "ms": round(kw["ms"], 5),
-        "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-        "frac": round(gbps / PEAK_HBM_GBPS, 4),
-        "algorithmic_bytes": kw["bytes"],
-    }
-    if not args.no_decode:
+    if "kvwrite" in phases:
+        kw = bench_kv_write(args, binding, torch, flush)
+        gbps = kw["bytes"] / (kw["ms"] * 1e-3) / 1e9
+        line["kv_write"] = {
+            "workload": "mla_kv_write: the 4096 new tokens of dsv3_prefill_4k, raw 576-wide "
+                        "rows normalised, rotated and stored into a bf16 pool of 128-row pages",
+            "ms": round(kw["ms"], 5), "median_ms": round(kw["median_ms"], 5),
+            "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "algorithmic_bytes": kw["bytes"],
+            "timing": "each call after reading a 1 GiB buffer (cache flush); a 10 MB call is latency-bound",
+            "graph_replay_ms_cached": round(kw["graph_ms"], 5),
+        }
+    if "unified" in phases:
         un = bench_unified(args, binding, torch)
         gbps = un["decode_bytes"] / (un["decode_ms"] * 1e-3) / 1e9
         line["prefill_decode"] = {
@@ -561,7 +886,12 @@ def main():
             "decode_achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "decode_frac": round(gbps / PEAK_HBM_GBPS, 4),
         }
-    if not args.no_cpu:
+    if "hbm" in phases:
+        del flush
+        torch.cuda.empty_cache()
+        line["hbm_ceiling"] = hbm_ceiling(binding, torch)
+        line["hbm_ceiling"]["spec_gbps"] = PEAK_HBM_GBPS
+    if "cpu" in phases:
         tf, sec, threads = cpu_baseline(p["wl"], args.cpu_heads)
         line["cpu_baseline"] = {
             "value": round(tf, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -570,7 +900,10 @@ def main():
                       f"heads; {sec:.1f} s; rate in attention FLOPs of the sample",
             "seconds": round(sec, 2),
             "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(),
         }
+        if ragged and dec_wl is not None:
+            line["cpu_baseline"]["other_workloads"] = oracle_timings(ragged, dec_wl)
     print(json.dumps(line), flush=True)
 
 

@@ -356,6 +356,16 @@ int mla_decode_noalloc(void* output, const void* q, const uint32_t* context_leng
                        int32_t max_context_len, int32_t num_partitions, float scale,
                        const float* attn_sink, hipStream_t stream);
 
+/*
+ * mla_hbm_read -- measurement helper, not part of the attention path: reads
+ * `bytes` (a multiple of 16, src 16-byte aligned) once with streaming 16-byte
+ * loads from `groups` workgroups of 256 threads and stores one XOR word per
+ * workgroup into out (uint32 [groups], device). Timing it gives the practical
+ * HBM read rate that the decode and gather rates are compared with.
+ */
+int mla_hbm_read(const void* src, size_t bytes, uint32_t* out, int32_t groups,
+                 hipStream_t stream);
+
 /* Text for a status code, and the message of the calling thread's last failure. */
 const char* mla_status_string(int status);
 const char* mla_last_error(void);

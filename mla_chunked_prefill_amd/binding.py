@@ -53,6 +53,7 @@ _SIGNATURES = {
     "mla_prefill_decode": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I,
                                 _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                 _F, _F, _P, _I, _P, _P, _I, _P, _S, _P]),
+    "mla_hbm_read": (_I, [_P, _S, _P, _I, _P]),
     "mla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mla_last_error": (ctypes.c_char_p, []),
 }
@@ -409,6 +410,14 @@ def mla_prefill_decode(output, q, input_row_offsets, cache_lengths, kv_cache, pa
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("mla_prefill_decode", st)
+
+
+def mla_hbm_read(src, out, groups: int, stream=None):
+    """Streaming read of the whole of src (a measurement helper)."""
+    _expect(out, torch.uint32, (groups,), "out")
+    st = load().mla_hbm_read(_ptr(src), src.numel() * src.element_size(), _ptr(out),
+                             int(groups), _stream(stream))
+    _check("mla_hbm_read", st)
 
 
 # ---------------------------------------------------------------------------

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 
-SOURCES = ["api.hip", "plan.hip", "gather.hip", "gemm.hip", "attn.hip", "decode.hip"]
+SOURCES = ["api.hip", "plan.hip", "gather.hip", "gemm.hip", "attn.hip", "decode.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -207,6 +207,14 @@ const char* mla_status_string(int status) {
 
 const char* mla_last_error(void) { return g_last_error; }
 
+int mla_hbm_read(const void* src, size_t bytes, uint32_t* out, int32_t groups,
+                 hipStream_t stream) {
+  if (!src || !out) return fail(MLA_ERR_INVALID_ARG, "mla_hbm_read: null pointer");
+  if (misaligned({src}) || bytes % 16 != 0 || bytes == 0 || groups < 1 || groups > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARG, "mla_hbm_read: bytes=%zu groups=%d", bytes, groups);
+  return hip_status(mla::launch_hbm_read(src, bytes, out, groups, stream), "read kernel");
+}
+
 int mla_prefill_plan(uint32_t* buffer_row_offsets, uint32_t* cache_offsets,
                      int32_t* buffer_lengths, uint32_t* chunks_needed,
                      const uint32_t* input_row_offsets, const uint32_t* cache_lengths,

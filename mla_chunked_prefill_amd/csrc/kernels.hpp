@@ -115,4 +115,7 @@ hipError_t launch_decode_split(const DecodeArgs&, bool, hipStream_t);
 hipError_t launch_decode_combine(const CombineArgs&, hipStream_t);
 hipError_t launch_decode_project(uint16_t*, const uint16_t*, const uint16_t*, int, int,
                                  hipStream_t);
+// streaming read of bytes (a multiple of 16) from src; one word per workgroup to out
+hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* out, int groups,
+                           hipStream_t stream);
 }  // namespace mla

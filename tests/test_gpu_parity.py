@@ -974,3 +974,20 @@ def test_unified_decode_at_full_size_matches_the_decode_entry(B):
                                          1e-6, 512)
         ref = np.concatenate([latn[0], kr[0]])
         assert (np.abs(got - ref) <= _stored_bound(ref, False)).all()
+
+
+def test_hbm_read_probe_folds_every_word(B):
+    """The measurement helper reads every 16-byte word once: each workgroup's
+    XOR equals the XOR of the words the grid-stride loop assigns to it."""
+    rng = np.random.default_rng(141)
+    for n16, groups in ((1000, 3), (256 * 40 + 7, 8), (1 << 16, 64)):
+        words = rng.integers(0, 2 ** 32, size=(n16, 4), dtype=np.uint64).astype(np.uint32)
+        src = torch.from_numpy(words.view(np.int32)).cuda()
+        out = torch.zeros(groups, dtype=torch.uint32, device="cuda")
+        B.mla_hbm_read(src, out, groups)
+        torch.cuda.synchronize()
+        owner = (np.arange(n16) % (groups * 256)) // 256
+        per_word = np.bitwise_xor.reduce(words, axis=1)
+        want = [int(np.bitwise_xor.reduce(per_word[owner == w])) if (owner == w).any() else 0
+                for w in range(groups)]
+        assert out.cpu().numpy().astype(np.int64).tolist() == want
