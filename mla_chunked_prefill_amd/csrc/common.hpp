@@ -100,4 +100,15 @@ __device__ __forceinline__ float sum_with_lane32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The same with the lane 16 away inside each 32-lane half
+// (v_permlane16_swap, gfx950).
+__device__ __forceinline__ float max_with_lane16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_lane16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace mla

@@ -14,6 +14,9 @@
 //               touched the sequence are merged by log-sum-exp into o_lat.
 //  4. project:  out[b, h] = w_uv[h] o_lat[b, h], bf16 MFMA, one wave per
 //               32 x 32 output tile.
+#include <array>
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace mla {
@@ -742,6 +745,440 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 
 
 // ---------------------------------------------------------------------------
+// 2'. split-KV attention over an e4m3 cache: both products on fp8 MFMA
+// ---------------------------------------------------------------------------
+// The same key ranges and partial states as the bf16 kernel; tiles of 64 keys
+// (36 KB of e4m3 rows, as stored) and v_mfma_f32_32x32x64_f8f6f4 for both
+// products, which runs at twice the rate of the bf16 instructions, so a byte
+// of cache costs the same matrix time as in the bf16 kernel. Wave w owns heads
+// 32 w .. 32 w + 31: per tile S^T = Z Q^T (2 key blocks x 9 depth steps of
+// 64) and O^T += Z^T P^T (16 dim blocks, one 64-key step).
+//  - q_abs is quantised per (sequence, head) to e4m3 when the segment starts:
+//    q / 2^e with 2^e the power of two that puts the head's largest |q| in
+//    (128, 256]; 2^e is folded into the score scale, so the scores are the
+//    e4m3 products accumulated in fp32 and rescaled exactly.
+//  - A lane's 32 fp8 values of an operand are depth (or key) 32 h + 0 .. 31 of
+//    its step, h = lane / 32, in both operands; the instruction sums over k
+//    in any order both operands share.
+//  - Key rows go to the score MFMA in the order kappa64 (block mb, row r ->
+//    key 32 ((r >> 2) & 1) + 16 mb + 4 (r >> 3) + (r & 3)), which makes a
+//    lane's 32 scores the keys 32 h .. 32 h + 31, in the order the value
+//    product's B operand (P^T) takes them.
+//  - Z^T is read with ds_read_b64_tr_b8: in each 16-lane group, lane i gets
+//    byte i % 8 of the 8 bytes that lanes i / 8, i / 8 + 2, .., i / 8 + 14
+//    address, so four reads give a lane 32 keys of one dim.
+//  - Probabilities are e4m3 as well: P = 2^(s - m + 7) against a reference
+//    maximum m per head that is raised (and O and the row sum rescaled) when a
+//    tile's maximum exceeds it by more than kF8Slack, so P stays below
+//    2^(7 + kF8Slack) < 448 and a weight 2^-16 of the maximum's is still
+//    represented.
+//  - Rows keep their 16-byte chunks with the low two index bits XORed by
+//    zf8swz(row), which puts the score reads (16 rows at one chunk) and the
+//    transposed reads (16 rows x 32 bytes) on distinct bank groups.
+constexpr int kF8BN = 64;                              // keys per tile
+constexpr int kF8TileB = kF8BN * kCache;               // 36864 bytes
+constexpr int kF8TStages = 4;
+constexpr int kF8TLoads = kF8TileB / 1024;             // 36 wave loads of 1 KB
+constexpr int kF8TLoadsPerWave = kF8TLoads / kDecWaves;  // 9
+constexpr int kF8RowChunks = kCache / 16;              // 36
+constexpr int kF8DSteps = kCache / 64;                 // 9 score steps
+constexpr float kF8Slack = 1.5f;
+constexpr float kF8Bias = 7.0f;
+static_assert(kF8TLoads % kDecWaves == 0, "even e4m3 loads per wave");
+static_assert(kF8TStages * kF8TileB <= kZStages * kZStageB, "staging fits");
+
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ int zf8swz(int row) { return ((row >> 2) & 1) | (((row >> 5) & 1) << 1); }
+__device__ __forceinline__ int zf8chunk(int row, int chunk) { return (chunk & ~3) | ((chunk & 3) ^ zf8swz(row)); }
+
+__device__ __forceinline__ u32x2 ds_read_tr8(const uint8_t* lds_byte_ptr) {
+  const auto v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(lds_byte_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__global__ void __launch_bounds__(kDecThreads, 1) decode_split_f8_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sZ[kF8TStages * kF8TileB];
+  __shared__ int sPT[kPTWindow];
+
+  const int w = blockIdx.x;
+  if (w >= a.G) return;
+  const uint32_t s_lo = a.wstart[w];
+  const uint32_t s_hi = a.wstart[w + 1];
+  if (s_lo >= s_hi) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int head = wave * 32 + l32;
+  const bool hvalid = head < a.H;
+  const uint8_t* cache = (const uint8_t*)a.cache;
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)sZ);
+
+  // ---- per-lane LDS read offsets (bytes inside a stage) ----
+  // scores, block mb, step ks: row kappa64(mb, l32), chunks 4 ks + 2 hf and
+  // 4 ks + 2 hf + 1 -> s_base[mb][0 or 1] + 64 ks
+  int s_base[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int row = 32 * ((l32 >> 2) & 1) + 16 * mb + 4 * (l32 >> 3) + (l32 & 3);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) s_base[mb][c] = row * kCache + zf8chunk(row, 2 * hf + c) * 16;
+  }
+  // transposed reads: dim block md, read q (keys 32 h + 8 q .. + 7), lane i
+  // of group G = lane / 16 (h = G / 2): source row 32 h + 8 q + i / 2, chunk
+  // 2 md + (G & 1), byte 8 (i & 1) -> tr_base[q][md & 1] + 64 (md >> 1)
+  uint32_t tr_pk[4];
+  {
+    const int G = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int m1 = 0; m1 < 2; ++m1) {
+        const int row = 32 * (G >> 1) + 8 * q + (i >> 1);
+        const uint32_t off = (uint32_t)(row * kCache + zf8chunk(row, 2 * m1 + (G & 1)) * 16 + 8 * (i & 1));
+        const int idx = q * 2 + m1;
+        if (idx & 1) tr_pk[idx >> 1] |= off << 16; else tr_pk[idx >> 1] = off;
+      }
+  }
+  auto tr_off = [&](int q, int md) __attribute__((always_inline)) {
+    const int idx = q * 2 + (md & 1);
+    return (int)((tr_pk[idx >> 1] >> (16 * (idx & 1))) & 0xFFFFu) + 64 * (md >> 1);
+  };
+  // direct loads of a contiguous tile: load j of this wave (p = wave + 4 j)
+  // fills LDS chunks 64 p + lane: tile row rr, source chunk zf8chunk(rr, cc)
+  uint32_t dma_pk[(kF8TLoadsPerWave + 1) / 2];
+#pragma unroll
+  for (int j = 0; j < kF8TLoadsPerWave; ++j) {
+    const int pch = (wave + kDecWaves * j) * 64 + lane;
+    const int rr = pch / kF8RowChunks;
+    const uint32_t off = (uint32_t)(rr * kCache + zf8chunk(rr, pch - rr * kF8RowChunks) * 16);
+    if (j & 1) dma_pk[j >> 1] |= off << 16; else dma_pk[j >> 1] = off;
+  }
+  auto dma_off = [&](int j) __attribute__((always_inline)) {
+    return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  };
+  const bool contiguous = (a.ps % kF8BN) == 0;
+
+  int b = a.wfirst[w];
+  uint32_t pos = s_lo;
+  while (pos < s_hi) {
+    const uint32_t seg_end = min(s_hi, a.cum[b + 1]);
+    if (seg_end <= pos) { ++b; continue; }
+    const int k0 = (int)(pos - a.cum[b]);
+    const int k1 = (int)(seg_end - a.cum[b]);
+    const int kt0 = k0 & ~(kF8BN - 1);
+    const int ntiles = (k1 - kt0 + kF8BN - 1) / kF8BN;
+    const int ctx_b = (int)(a.cum[b + 1] - a.cum[b]);
+    const int lp0 = kt0 / a.ps;
+    const int npg = (k1 - 1) / a.ps - lp0 + 1;
+    // this lane's half of its head's absorbed query: depth 64 ks + 32 hf + 0..31
+    u32x4 qraw[kF8DSteps][4];
+    {
+      const uint16_t* qrow = a.q_abs + ((size_t)b * a.H + min(head, a.H - 1)) * kCache + hf * 32;
+#pragma unroll
+      for (int ks = 0; ks < kF8DSteps; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          qraw[ks][c] = hvalid ? *(const u32x4*)(qrow + ks * 64 + c * 8) : u32x4{0, 0, 0, 0};
+    }
+    auto pt_entry = [&](int e) __attribute__((always_inline)) {
+      const int lp = lp0 + e;
+      const int v = (e < npg && lp < a.maxp) ? a.page_table[(size_t)b * a.maxp + lp] : 0;
+      return (v < 0 || v >= a.num_pages) ? 0 : v;
+    };
+    int pg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pg[i] = pt_entry(tid + kDecThreads * i);
+    __syncthreads();  // the previous segment is done with the page window and the stages
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sPT[tid + kDecThreads * i] = pg[i];
+#pragma unroll
+    for (int i = 2; i < kPTWindow / kDecThreads; ++i)
+      sPT[tid + kDecThreads * i] = pt_entry(tid + kDecThreads * i);
+    __syncthreads();  // page window written
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // q and the page table in registers (vmcnt 0)
+
+    // quantise the head's query to e4m3 with a power-of-two scale 2^qe
+    i32x8 qf[kF8DSteps];
+    float sl2;  // scale * log2(e) * 2^qe: converts q8 . z8 to log2 units
+    {
+      float amax = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kF8DSteps; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qraw[ks][c][e])), fabsf(bf16_hi(qraw[ks][c][e]))));
+      amax = max_with_lane32(amax);
+      // amax * 2^-qe in (128, 256]; a zero query keeps qe = 0
+      const int qe = amax > 0.f ? (int)ceilf(__builtin_amdgcn_logf(amax)) - 8 : 0;
+      const float inv = __builtin_amdgcn_ldexpf(1.0f, -qe);
+      sl2 = a.scale_log2 * __builtin_amdgcn_ldexpf(1.0f, qe);
+#pragma unroll
+      for (int ks = 0; ks < kF8DSteps; ++ks)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint32_t w0 = 0, w1 = 0;
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(qraw[ks][c][0]) * inv, bf16_hi(qraw[ks][c][0]) * inv, w0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(qraw[ks][c][1]) * inv, bf16_hi(qraw[ks][c][1]) * inv, w0, true);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(qraw[ks][c][2]) * inv, bf16_hi(qraw[ks][c][2]) * inv, w1, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(qraw[ks][c][3]) * inv, bf16_hi(qraw[ks][c][3]) * inv, w1, true);
+          qf[ks][2 * c] = (int)w0;
+          qf[ks][2 * c + 1] = (int)w1;
+        }
+    }
+
+    auto slot_of = [&](int key) __attribute__((always_inline)) {
+      const int lp = key / a.ps;
+      return sPT[min(lp - lp0, kPTWindow - 1)] * a.ps + (key - lp * a.ps);
+    };
+    auto one_piece = [&](int t) __attribute__((always_inline)) {
+      return contiguous && kt0 + (t + 1) * kF8BN <= ctx_b;
+    };
+    auto issue = [&](int t) __attribute__((always_inline)) {
+      const int kt = kt0 + t * kF8BN;
+      const uint32_t base = lds0 + (t % kF8TStages) * kF8TileB;
+      if (one_piece(t)) {
+        const void* sb = uniform_ptr_d(cache + (size_t)slot_of(kt) * kCache);
+#pragma unroll
+        for (int j = 0; j < kF8TLoadsPerWave; ++j)
+          dma16_s_nb(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+        asm volatile("" ::: "memory");
+      } else {
+        // pool slot of tile row `lane`; rows past the segment read its last row
+        const int slot = slot_of(min(kt + lane, k1 - 1));
+#pragma unroll 1
+        for (int p = wave; p < kF8TLoads; p += kDecWaves) {
+          const int pch = p * 64 + lane;
+          const int rr = pch / kF8RowChunks;
+          const int rs = __shfl(slot, rr, 64);
+          dma16(cache + (size_t)rs * kCache + zf8chunk(rr, pch - rr * kF8RowChunks) * 16,
+                base + p * 1024);
+        }
+      }
+    };
+
+    f32x16 o[16];
+#pragma unroll
+    for (int md = 0; md < 16; ++md)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[md][i] = 0.f;
+    float m_ref = -INFINITY;  // reference maximum of this head (log2 domain)
+    float l_run = 0.f;        // this lane's share of the row sum, in units of 2^(m_ref - 7)
+
+    for (int t = 0; t < min(2, ntiles); ++t) issue(t);
+
+    auto scores_t = [&](const uint8_t* Zs, const void* sbn, uint32_t nbase, auto with_dma)
+        __attribute__((always_inline)) {
+      std::array<f32x16, 2> acc;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+      constexpr int kAhead = 2;
+      constexpr int kSteps = 2 * kF8DSteps;  // 18: (ks, mb) pairs
+      i32x8 zb[kAhead];
+      auto zload = [&](int i) __attribute__((always_inline)) {
+        const int ks = i >> 1, mb = i & 1;
+        const u32x4 lo = *(const u32x4*)(Zs + s_base[mb][0] + 64 * ks);
+        const u32x4 hi = *(const u32x4*)(Zs + s_base[mb][1] + 64 * ks);
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) zb[i] = zload(i);
+#pragma unroll
+      for (int i = 0; i < kSteps; ++i) {
+        acc[i & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(zb[i % kAhead], qf[i >> 1],
+                                                                     acc[i & 1], 0, 0, 0, 0, 0, 0);
+        if (i + kAhead < kSteps) zb[i % kAhead] = zload(i + kAhead);
+        if constexpr (decltype(with_dma)::value) {
+          if ((i & 1) == 0 && i / 2 < kF8TLoadsPerWave)
+            dma16_s_nb(sbn, dma_off(i / 2), nbase + (wave + kDecWaves * (i / 2)) * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return acc;
+    };
+    // O^T[512 dims x 32 heads] += Z^T P^T, fragments two MFMAs ahead; piece(i)
+    // runs after MFMA i
+    auto value_product = [&](const uint8_t* Zv, const i32x8& pb, auto piece)
+        __attribute__((always_inline)) {
+      constexpr int kAhead = 2;
+      i32x8 vb[kAhead];
+      auto vload = [&](int md) __attribute__((always_inline)) {
+        const u32x2 r0 = ds_read_tr8(Zv + tr_off(0, md));
+        const u32x2 r1 = ds_read_tr8(Zv + tr_off(1, md));
+        const u32x2 r2 = ds_read_tr8(Zv + tr_off(2, md));
+        const u32x2 r3 = ds_read_tr8(Zv + tr_off(3, md));
+        return i32x8{(int)r0[0], (int)r0[1], (int)r1[0], (int)r1[1],
+                     (int)r2[0], (int)r2[1], (int)r3[0], (int)r3[1]};
+      };
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) vb[i] = vload(i);
+#pragma unroll
+      for (int md = 0; md < 16; ++md) {
+        o[md] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[md % kAhead], pb, o[md], 0, 0,
+                                                                0, 0, 0, 0);
+        if (md + kAhead < 16) vb[md % kAhead] = vload(md + kAhead);
+        piece(md);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // softmax pieces of one tile: 0, 1 the tile maximum; 2 the head's maximum
+    // and the growth test; 4, 5, .., 11 four probabilities each
+    float tmax = -INFINITY, mt = -INFINITY, neg_m = 0.f, psum = 0.f;
+    bool grow = false;
+    uint32_t pw[8];
+    auto prob4 = [&](const std::array<f32x16, 2>& sc, int j) __attribute__((always_inline)) {
+      // bytes 4 j .. 4 j + 3 of the lane's 32: block j / 4, registers 4 (j % 4) ..
+      const f32x16& v = sc[j >> 2];
+      const int r = 4 * (j & 3);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(v[r], sl2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(v[r + 1], sl2, neg_m));
+      const float p2 = __builtin_amdgcn_exp2f(fmaf(v[r + 2], sl2, neg_m));
+      const float p3 = __builtin_amdgcn_exp2f(fmaf(v[r + 3], sl2, neg_m));
+      uint32_t x = 0;
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, x, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+      pw[j] = x;
+      psum += (p0 + p1) + (p2 + p3);
+    };
+    auto softmax_piece = [&](const std::array<f32x16, 2>& sc, int i, bool first)
+        __attribute__((always_inline)) {
+      if (i == 0) {
+        tmax = sc[0][0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) tmax = fmaxf(tmax, sc[0][k]);
+      } else if (i == 1) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) tmax = fmaxf(tmax, sc[1][k]);
+      } else if (i == 2) {
+        mt = max_with_lane32(tmax * sl2);  // the head's tile maximum; -inf if all masked
+        if (first) m_ref = mt;             // finite: the first tile holds a valid key
+        grow = __ballot(mt > m_ref + kF8Slack) != 0;
+        neg_m = kF8Bias - m_ref;
+        psum = 0.f;
+      } else if (i >= 4 && i < 12) {
+        if (!grow) prob4(sc, i - 4);
+      }
+    };
+    // after the value product that used the previous reference: raise the
+    // reference to the tile maximum where it grew, rescale, recompute P
+    auto settle = [&](const std::array<f32x16, 2>& sc) __attribute__((always_inline)) {
+      if (grow) {
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= alpha;
+        // in place in the accumulation registers, one value at a time (the
+        // compiler would otherwise move the 256 accumulators through vector
+        // registers and spill)
+#pragma unroll
+        for (int md = 0; md < 16; ++md)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float tmp;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1"
+                : "+a"(o[md][i]), "=&v"(tmp)
+                : "v"(alpha));
+          }
+        m_ref = m_new;
+        neg_m = kF8Bias - m_ref;
+        psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) prob4(sc, j);
+        grow = false;
+      }
+      l_run += psum;
+    };
+    i32x8 pprev;
+    auto take_probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pprev[j] = (int)pw[j];
+    };
+
+    auto front = [&](int t) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      static_assert(kF8TLoadsPerWave == 9, "wait counts");
+      // the packed offsets stay packed (unpacked per use, not kept unpacked
+      // across the loop, where they would not fit the registers)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(tr_pk[k]));
+#pragma unroll
+      for (int k = 0; k < (kF8TLoadsPerWave + 1) / 2; ++k) asm volatile("" : "+v"(dma_pk[k]));
+      __syncthreads();
+      const bool spread = t + 2 < ntiles && one_piece(t + 2);
+      const void* sbn = cache;
+      if (spread) sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 2) * kF8BN) * kCache);
+      else if (t + 2 < ntiles) issue(t + 2);
+      const uint32_t nbase = lds0 + ((t + 2) % kF8TStages) * kF8TileB;
+      const uint8_t* Z = sZ + (t % kF8TStages) * kF8TileB;
+      const int kt = kt0 + t * kF8BN;
+      std::array<f32x16, 2> s = spread ? scores_t(Z, sbn, nbase, std::integral_constant<bool, true>())
+                                       : scores_t(Z, sbn, nbase, std::integral_constant<bool, false>());
+      // register i of block mb holds key kt + 32 hf + 16 mb + i
+      if (kt < k0 || kt + kF8BN > k1) {
+        const int lo = k0 - kt - 32 * hf, hi = k1 - kt - 32 * hf;  // valid: lo <= c < hi
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = 16 * mb + i;
+            if (c < lo || c >= hi) s[mb][i] = -INFINITY;
+          }
+      }
+      return s;
+    };
+    {
+      const std::array<f32x16, 2> s = front(0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) softmax_piece(s, i, true);
+      settle(s);
+      take_probs();
+    }
+    for (int t = 1; t < ntiles; ++t) {
+      const std::array<f32x16, 2> s = front(t);
+      value_product(sZ + ((t - 1) % kF8TStages) * kF8TileB, pprev,
+                    [&](int i) __attribute__((always_inline)) { softmax_piece(s, i, false); });
+      settle(s);
+      take_probs();
+    }
+    value_product(sZ + ((ntiles - 1) % kF8TStages) * kF8TileB, pprev,
+                  [&](int) __attribute__((always_inline)) {});
+    l_run = sum_with_lane32(l_run);
+    if (hvalid) {
+      const size_t base = ((size_t)(w + b) * a.H + head);
+      // O^T register i of block md: dim 32 md + 8 (i / 4) + 4 hf + i % 4
+      float* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
+#pragma unroll
+      for (int md = 0; md < 16; ++md)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
+          *(f32x4*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
+        }
+      if (hf == 0) {
+        a.part_ml[base * 2 + 0] = m_ref - kF8Bias;
+        a.part_ml[base * 2 + 1] = l_run;
+      }
+    }
+    pos = seg_end;
+    ++b;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. combine the partial states: o_lat[b, h, :] (bf16 hi + lo)
 // ---------------------------------------------------------------------------
 // One wave per (sequence, head), lane l owns dims 8 l .. 8 l + 7: the maximum
@@ -966,7 +1403,7 @@ hipError_t launch_decode_absorb(uint16_t* q_abs, const uint16_t* q, const uint16
 
 hipError_t launch_decode_split(const DecodeArgs& a, bool fp8, hipStream_t stream) {
   if (fp8)
-    hipLaunchKernelGGL(decode_split_kernel<true>, dim3(a.G), dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_f8_kernel, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
