@@ -312,8 +312,11 @@ int mla_prefill(void* output, const void* q, int32_t dtype,
  *   device value counts as max_context_len; its result is unspecified)
  *   Limits: num_heads <= 128; batch_size * max_context_len < 2^31;
  *   num_pages * page_size < 2^31.
- * With an e4m3 cache the rows are widened exactly to bf16 (every e4m3fn value
- * is a bf16 number) and both products run on bf16 MFMA with a bf16 q_lat.
+ * With an e4m3 cache both products run on fp8 MFMA: the absorbed query is
+ * quantised per (sequence, head) to e4m3 under a power-of-two scale folded
+ * into the score scale, and the probabilities are e4m3 values 2^(s - m + 7)
+ * against a running maximum m per head (raised, with the partial output
+ * rescaled, whenever a tile's scores exceed it by more than 1.5 log2 units).
  */
 size_t mla_decode_workspace_size(int32_t batch_size, int32_t num_heads,
                                  int32_t max_context_len, int32_t page_size,

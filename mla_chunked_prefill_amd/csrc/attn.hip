@@ -44,7 +44,7 @@ namespace mla {
 constexpr int kAttnBM = 128;  // queries per workgroup
 constexpr int kAttnBN = 64;   // keys per tile
 
-typedef long fp8x8;  // 8 e4m3 values in one 64-bit register pair
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));  // 32 e4m3 values
 
 // Rescale the output accumulator only when a query's running maximum grows by
 // more than this many (log2) units; in between, probabilities are formed
@@ -82,6 +82,13 @@ template <int kChunks>
 __device__ __forceinline__ int swz_rows(int r) {
   return kChunks >= 16 ? swz4(r) : (kChunks == 8 ? swz3(r) : (swz3(r) & 3));
 }
+// e4m3 rows (K_nope 128 bytes = 8 chunks, k_rope 64 bytes = 4 chunks), read
+// 32 bytes per lane by the fp8 score MFMA: the 16 rows a read serves at once
+// land on distinct 16-byte bank groups
+template <int kChunks>
+__device__ __forceinline__ int swz_rows_f8(int r) {
+  return kChunks == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes, read from
 // sbase + voff, land at LDS byte address lds + 16 l (lds and sbase are
@@ -106,11 +113,11 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // Per-lane source offset (bytes, inside a tile) of direct load `i` of a region
 // whose LDS rows hold kChunks 16-byte chunks and whose global rows are
 // `gstride` bytes apart (kValue: the value tile's permutation).
-template <int kChunks, bool kValue = false>
+template <int kChunks, bool kValue = false, bool kF8 = false>
 __device__ __forceinline__ uint32_t dma_src(int i, int lane, uint32_t gstride) {
   const int p = i * 64 + lane;
   const int r = p / kChunks;
-  const int j = (p % kChunks) ^ (kValue ? swzv(r) : swz_rows<kChunks>(r));
+  const int j = (p % kChunks) ^ (kValue ? swzv(r) : (kF8 ? swz_rows_f8<kChunks>(r) : swz_rows<kChunks>(r)));
   return (uint32_t)r * gstride + (uint32_t)j * 16u;
 }
 
@@ -166,13 +173,18 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   const int w_all_hi = r0 + min(len - 1, c_b + wq_lo - co);     // may be < r0
   const int w_any_hi = r0 + min(len - 1, c_b + wq_hi - 1 - co);
 
-  // Q fragments: B operand of S^T = K Q^T (lane: query l32, depth 8*hf + 16*ks ..)
+  // Q fragments: B operand of S^T = K Q^T (lane: query l32; bf16: depth
+  // 16 ks + 8 hf .. + 7; e4m3: depth 64 ks + 32 hf .. + 31 for the fp8 MFMA)
   bf16x8 qf[12];
-  fp8x8 qf8[12];
+  i32x8 qf8[3];
   if (kFp8) {
-    const uint8_t* qp = (const uint8_t*)a.q + (t * a.H + h) * kQDepth + hf * 8;
+    const uint8_t* qp = (const uint8_t*)a.q + (t * a.H + h) * kQDepth + hf * 32;
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) qf8[ks] = qvalid ? *(const fp8x8*)(qp + ks * 16) : 0;
+    for (int ks = 0; ks < 3; ++ks) {
+      const u32x4 lo = qvalid ? *(const u32x4*)(qp + ks * 64) : u32x4{0, 0, 0, 0};
+      const u32x4 hi = qvalid ? *(const u32x4*)(qp + ks * 64 + 16) : u32x4{0, 0, 0, 0};
+      qf8[ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   } else {
     const uint16_t* qp = (const uint16_t*)a.q + (t * a.H + h) * kQDepth + hf * 8;
 #pragma unroll
@@ -208,16 +220,21 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   const int kappa = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   constexpr int kNopeC = L::kNopeRowB / 16;
   constexpr int kRopeC = L::kRopeRowB / 16;
+  // bf16: nb[ks] / rb[ks] read 16 bytes of step ks; e4m3: nb[2 ks + c] /
+  // rb[c] read chunk 4 ks + 2 hf + c (nope) or 2 hf + c (rope) of row kappa
   int nb[8], rb[4], vb[4];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    if (kFp8) nb[kk] = kappa * L::kNopeRowB + ((kk ^ swz_rows<kNopeC>(kappa)) * 16) + hf * 8;
+    if (kFp8)
+      nb[kk] = kappa * L::kNopeRowB +
+               (((4 * (kk >> 1) + 2 * hf + (kk & 1)) ^ swz_rows_f8<kNopeC>(kappa)) * 16);
     else nb[kk] = kappa * L::kNopeRowB + (((2 * kk + hf) ^ swz_rows<kNopeC>(kappa)) * 16);
   }
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     if (kFp8)
-      rb[kk] = L::kRopeOff + kappa * L::kRopeRowB + ((kk ^ swz_rows<kRopeC>(kappa)) * 16) + hf * 8;
+      rb[kk] = L::kRopeOff + kappa * L::kRopeRowB +
+               (((2 * hf + (kk & 1)) ^ swz_rows_f8<kRopeC>(kappa)) * 16);
     else
       rb[kk] = L::kRopeOff + kappa * L::kRopeRowB + (((2 * kk + hf) ^ swz_rows<kRopeC>(kappa)) * 16);
     vb[kk] = L::kVOff + l32 * L::kVRowB + (((2 * kk + hf) ^ swzv(l32)) * 16);
@@ -227,10 +244,10 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
   uint32_t src_n[L::kNopeLoads], src_r[L::kRopeLoads], src_v[L::kVLoads];
 #pragma unroll
   for (int k = 0; k < L::kNopeLoads; ++k)
-    src_n[k] = dma_src<kNopeC>(wave + 4 * k, lane, L::kNopeRowB);
+    src_n[k] = dma_src<kNopeC, false, kFp8>(wave + 4 * k, lane, L::kNopeRowB);
 #pragma unroll
   for (int k = 0; k < L::kRopeLoads; ++k)
-    src_r[k] = dma_src<kRopeC>(wave + 4 * k, lane, L::kRopeRowB);
+    src_r[k] = dma_src<kRopeC, false, kFp8>(wave + 4 * k, lane, L::kRopeRowB);
 #pragma unroll
   for (int k = 0; k < L::kVLoads; ++k)
     src_v[k] = dma_src<8, true>(wave + 4 * k, lane, (uint32_t)a.max_rows * 2u);
@@ -277,16 +294,28 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
+    if (kFp8) {
+      // three 64-deep steps (nope 0..63, nope 64..127, rope) on
+      // v_mfma_f32_32x32x64_f8f6f4, twice the rate of the 16-deep fp8 form
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks) {
+      for (int ks = 0; ks < 3; ++ks) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int off = ks < 8 ? nb[ks] + mb * 32 * L::kNopeRowB
-                               : rb[ks - 8] + mb * 32 * L::kRopeRowB;
-        if (kFp8) {
-          const fp8x8 ka = *(const fp8x8*)(st + off);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ka, qf8[ks], s[mb], 0, 0, 0);
-        } else {
+        for (int mb = 0; mb < 2; ++mb) {
+          const int o0 = ks < 2 ? nb[2 * ks] + mb * 32 * L::kNopeRowB : rb[0] + mb * 32 * L::kRopeRowB;
+          const int o1 = ks < 2 ? nb[2 * ks + 1] + mb * 32 * L::kNopeRowB : rb[1] + mb * 32 * L::kRopeRowB;
+          const u32x4 lo = *(const u32x4*)(st + o0);
+          const u32x4 hi = *(const u32x4*)(st + o1);
+          const i32x8 ka = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          s[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf8[ks], s[mb], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int off = ks < 8 ? nb[ks] + mb * 32 * L::kNopeRowB
+                                 : rb[ks - 8] + mb * 32 * L::kRopeRowB;
           const bf16x8 ka = *(const bf16x8*)(st + off);
           s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[mb], 0, 0, 0);
         }

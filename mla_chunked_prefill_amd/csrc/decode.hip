@@ -293,17 +293,13 @@ __global__ void __launch_bounds__(256) head_gemm_kernel(
 // t's scores, then tile t-1's value product with tile t's softmax placed
 // between its MFMAs (those MFMAs wait on LDS reads, which leaves room for the
 // vector work); the loads of tile t+2 go out while tile t's scores are
-// computed. bf16: four stages hold tiles t-1 .. t+2. When the page size is a multiple of 32 a tile is 32
-// consecutive pool rows (36 KB in one piece, 18 KB for e4m3) and its direct
-// loads are spread between the score MFMAs; otherwise every row's pool slot
-// is looked up and the loads go out in one burst. A bf16 row keeps its 72
-// 16-byte chunks with the chunk index's low three bits XORed by zswz(row), so
-// the score reads (16 rows at one column) and the transposed reads (4 rows x
-// 64 bytes) touch distinct LDS banks. An e4m3 tile lands, rows as stored, in
-// one of two load stages; at the end of iteration t every wave widens
-// exactly the bytes its own loads of tile t+1 brought into the third of
-// three bf16 stages (the other two hold tiles t-1 and t), so the one barrier
-// per tile also publishes the widened tile.
+// computed. Four stages hold tiles t-1 .. t+2. When the page size is a
+// multiple of 32 a tile is 32 consecutive pool rows (36 KB in one piece) and
+// its direct loads are spread between the score MFMAs; otherwise every row's
+// pool slot is looked up and the loads go out in one burst. A row keeps its
+// 72 16-byte chunks with the chunk index's low three bits XORed by zswz(row),
+// so the score reads (16 rows at one column) and the transposed reads (4 rows
+// x 64 bytes) touch distinct LDS banks.
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecBN = 32;                          // keys per tile
@@ -316,16 +312,7 @@ constexpr int kZLoadsPerWave = kZLoads / kDecWaves; // 9
 constexpr int kPTWindow = kDecPageWindow;           // page-table entries staged per segment
 constexpr int kQSteps = kCache / 16;                // 36 score steps
 constexpr float kDecSlack = 64.0f;
-// e4m3 cache: rows kept as stored in the staging buffers
-constexpr int kF8RowB = kCache;                     // 576 bytes
-constexpr int kF8StageB = kDecBN * kF8RowB;         // 18432 bytes
-constexpr int kF8Stages = 2;                        // e4m3 tiles as stored
-constexpr int kZStagesF8 = 3;                       // e4m3: bf16 stages the tiles are widened into
-constexpr int kF8Loads = kF8StageB / 1024;          // 18 wave loads of 1 KB
-constexpr int kF8LoadsPerWave = (kF8Loads + kDecWaves - 1) / kDecWaves;  // 5 (waves 2, 3: 4)
 static_assert(kZLoads % kDecWaves == 0, "even bf16 loads per wave");
-static_assert(kF8Loads == 4 * kDecWaves + 2, "e4m3: waves 0, 1 load five times, waves 2, 3 four");
-static_assert(kZStagesF8 * kZStageB + kF8Stages * kF8StageB <= kZStages * kZStageB, "staging fits");
 static_assert(kPTWindow % kDecThreads == 0, "even page-table staging per thread");
 
 // XOR applied to the low three bits of a row's 16-byte chunk index
@@ -369,27 +356,9 @@ __device__ __forceinline__ const void* uniform_ptr_d(const void* p) {
   return (const void*)(((uint64_t)hi << 32) | lo);
 }
 
-// 8 e4m3fn codes -> 8 bf16 values (exact: every e4m3fn value, subnormals
-// included, is a bf16 normal number or zero)
-__device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 v) {
-  u32x4 o;
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true));
-  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false));
-  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true));
-  return o;
-}
-
-template <bool kFp8>
 __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs a) {
-  // bf16: four stages; e4m3: three bf16 stages and two load stages behind them
   __shared__ __attribute__((aligned(1024))) uint8_t sZ[kZStages * kZStageB];
   __shared__ int sPT[kPTWindow];
-  constexpr int kLoadsPerWave = kFp8 ? kF8LoadsPerWave : kZLoadsPerWave;
-  constexpr int kStageB = kFp8 ? kF8StageB : kZStageB;
-  constexpr int kStage0 = kFp8 ? kZStagesF8 * kZStageB : 0;  // byte offset of load stage 0
-  constexpr int kLoadStages = kFp8 ? kF8Stages : kZStages;
-  constexpr int kBfStages = kFp8 ? kZStagesF8 : kZStages;
 
   const int w = blockIdx.x;
   if (w >= a.G) return;
@@ -428,10 +397,10 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
       const int chunk = 4 * pm + 2 * (g16 & 1) + ((L16 >> 1) & 1);
       tr_base[t][pm] = row * kZRowB + zchunk(row, chunk) * 16 + (L16 & 1) * 8;
     }
-  // direct loads of a contiguous bf16 tile: load j of this wave (p = wave +
-  // 4 j) fills LDS chunks 64 p + lane, i.e. tile row rr, source chunk
-  // zchunk(rr, cc) (the XOR is its own inverse); byte offsets below 36 KB,
-  // two per register. e4m3: load p covers bytes 1024 p + 16 lane as stored.
+  // direct loads of a contiguous tile: load j of this wave (p = wave + 4 j)
+  // fills LDS chunks 64 p + lane, i.e. tile row rr, source chunk zchunk(rr,
+  // cc) (the XOR is its own inverse); byte offsets below 36 KB, two per
+  // register
   uint32_t dma_pk[(kZLoadsPerWave + 1) / 2];
 #pragma unroll
   for (int j = 0; j < kZLoadsPerWave; ++j) {
@@ -441,8 +410,7 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     if (j & 1) dma_pk[j >> 1] |= off << 16; else dma_pk[j >> 1] = off;
   }
   auto dma_off = [&](int j) __attribute__((always_inline)) {
-    if constexpr (kFp8) return (uint32_t)((wave + kDecWaves * j) * 1024 + lane * 16);
-    else return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    return (dma_pk[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
   };
   const bool contiguous = (a.ps % kDecBN) == 0;
 
@@ -501,16 +469,15 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     auto one_piece = [&](int t) __attribute__((always_inline)) {
       return contiguous && kt0 + (t + 1) * kDecBN <= ctx_b;
     };
-    // all loads of tile t into load stage t % 4, in one burst
+    // all loads of tile t into stage t % 4, in one burst
     auto issue = [&](int t) __attribute__((always_inline)) {
       const int kt = kt0 + t * kDecBN;
-      const uint32_t base = lds0 + kStage0 + (t % kLoadStages) * kStageB;
+      const uint32_t base = lds0 + (t % kZStages) * kZStageB;
       if (one_piece(t)) {
-        const void* sb = uniform_ptr_d(cache + (size_t)slot_of(kt) * (kFp8 ? kF8RowB : kZRowB));
+        const void* sb = uniform_ptr_d(cache + (size_t)slot_of(kt) * kZRowB);
 #pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j)
-          if (!kFp8 || wave + kDecWaves * j < kF8Loads)
-            dma16_s_nb(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
+        for (int j = 0; j < kZLoadsPerWave; ++j)
+          dma16_s_nb(sb, dma_off(j), base + (wave + kDecWaves * j) * 1024);
         asm volatile("" ::: "memory");
       } else {
         // pool slot of tile row (lane & 31); rows past the segment read its last
@@ -518,19 +485,12 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
         // at a time keeps this rarely taken path's registers few.
         const int slot = slot_of(min(kt + (lane & 31), k1 - 1));
 #pragma unroll 1
-        for (int p = wave; p < (kFp8 ? kF8Loads : kZLoads); p += kDecWaves) {
-          if constexpr (kFp8) {
-            const int byte = p * 1024 + lane * 16;
-            const int rr = byte / kF8RowB;
-            const int rs = __shfl(slot, rr, 64);
-            dma16(cache + (size_t)rs * kF8RowB + (byte - rr * kF8RowB), base + p * 1024);
-          } else {
-            const int pch = p * 64 + lane;
-            const int rr = pch / kZRowChunks;
-            const int rs = __shfl(slot, rr, 64);
-            dma16(cache + (size_t)rs * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16,
-                  base + p * 1024);
-          }
+        for (int p = wave; p < kZLoads; p += kDecWaves) {
+          const int pch = p * 64 + lane;
+          const int rr = pch / kZRowChunks;
+          const int rs = __shfl(slot, rr, 64);
+          dma16(cache + (size_t)rs * kZRowB + zchunk(rr, pch - rr * kZRowChunks) * 16,
+                base + p * 1024);
         }
       }
     };
@@ -547,40 +507,10 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 
     // tile t's scores, then tile t-1's value product with tile t's softmax
     // interleaved between its MFMAs (the value MFMAs wait on LDS reads; the
-    // softmax fills those gaps). bf16 stages hold tiles t-1 (value
-    // product), t (scores), t+1 and t+2 (loads in flight): the loads of
-    // tile t+2 go out once the barrier of tile t shows every wave done
-    // with tile t-2. e4m3: three bf16 stages hold tiles t-1, t and t+1,
-    // the last widened at the end of iteration t from its load stage.
+    // softmax fills those gaps). The stages hold tiles t-1 (value product),
+    // t (scores), t+1 and t+2 (loads in flight): the loads of tile t+2 go
+    // out once the barrier of tile t shows every wave done with tile t-2.
     for (int t = 0; t < min(2, ntiles); ++t) issue(t);
-    // e4m3: each wave waits for its own loads of tile tt and widens exactly
-    // the bytes they brought (load p: bytes 1024 p + 16 lane, 16 codes of
-    // one row) into bf16 stage tt % 3; the barrier at the top of the tile
-    // loop then publishes the whole tile. later: tiles issued after tt whose
-    // loads may stay in flight.
-    auto widen_own = [&](int tt, int later) __attribute__((always_inline)) {
-      if (later == 1) {
-        if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      const uint8_t* F = sZ + kStage0 + (tt % kF8Stages) * kF8StageB;
-      uint8_t* D = sZ + (tt % kZStagesF8) * kZStageB;
-#pragma unroll
-      for (int j = 0; j < kF8LoadsPerWave; ++j) {
-        const int p = wave + kDecWaves * j;
-        if (p < kF8Loads) {
-          const int byte = p * 1024 + lane * 16;
-          const int r = byte / kF8RowB;
-          const int c = (byte - r * kF8RowB) / 8;  // first of two bf16 chunks
-          const u32x4 v = *(const u32x4*)(F + byte);
-          *(u32x4*)(D + r * kZRowB + zchunk(r, c) * 16) = widen_e4m3x8(u32x2{v[0], v[1]});
-          *(u32x4*)(D + r * kZRowB + zchunk(r, c + 1) * 16) = widen_e4m3x8(u32x2{v[2], v[3]});
-        }
-      }
-    };
-    if constexpr (kFp8) widen_own(0, min(1, ntiles - 1));
     auto scores_t = [&](const uint8_t* Zs, const void* sbn, uint32_t nbase, auto with_dma)
         __attribute__((always_inline)) {
       f32x16 acc;
@@ -666,23 +596,19 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     // wait for tile t, publish it, send tile t+2's loads, compute and mask
     // tile t's scores
     auto front = [&](int t) __attribute__((always_inline)) {
-      // this wave's loads of tile t are done (those of tile t+1 may not be;
-      // e4m3: the wave widened its part of tile t already)
-      if constexpr (!kFp8) {
-        if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      static_assert(kZLoadsPerWave == 9 && kF8LoadsPerWave == 5, "wait counts");
+      // this wave's loads of tile t are done (those of tile t+1 may not be)
+      if (t + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      static_assert(kZLoadsPerWave == 9, "wait counts");
       // tile t is in place for every wave; every wave is done with tile
-      // t-2, whose stage receives tile t+2 (e4m3: with tile t, whose load
-      // stage receives tile t+2)
+      // t-2, whose stage receives tile t+2
       __syncthreads();
-      const bool spread = !kFp8 && t + 2 < ntiles && one_piece(t + 2);
+      const bool spread = t + 2 < ntiles && one_piece(t + 2);
       const void* sbn = cache;
       if (spread) sbn = uniform_ptr_d(cache + (size_t)slot_of(kt0 + (t + 2) * kDecBN) * kZRowB);
       else if (t + 2 < ntiles) issue(t + 2);
       const uint32_t nbase = lds0 + ((t + 2) % 4) * kZStageB;
-      const uint8_t* Z = sZ + (t % kBfStages) * kZStageB;
+      const uint8_t* Z = sZ + (t % kZStages) * kZStageB;
       const int kt = kt0 + t * kDecBN;
       f32x16 s = spread ? scores_t(Z, sbn, nbase, std::integral_constant<bool, true>())
                         : scores_t(Z, sbn, nbase, std::integral_constant<bool, false>());
@@ -702,18 +628,14 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int i = 0; i <= 20; ++i) softmax_piece(s, i, true);
       take_probs();
-      if constexpr (kFp8)
-        if (1 < ntiles) widen_own(1, min(1, ntiles - 2));
     }
     for (int t = 1; t < ntiles; ++t) {
       const f32x16 s = front(t);
-      value_product(sZ + ((t - 1) % kBfStages) * kZStageB, pprev,
+      value_product(sZ + ((t - 1) % kZStages) * kZStageB, pprev,
                     [&](int i) __attribute__((always_inline)) { softmax_piece(s, i, false); });
       take_probs();
-      if constexpr (kFp8)
-        if (t + 1 < ntiles) widen_own(t + 1, min(1, ntiles - 2 - t));
     }
-    value_product(sZ + ((ntiles - 1) % kBfStages) * kZStageB, pprev,
+    value_product(sZ + ((ntiles - 1) % kZStages) * kZStageB, pprev,
                   [&](int) __attribute__((always_inline)) {});
     // partial state of (w, b): slot w + b. The output is stored by groups of
     // eight dims, [slot][dim / 8][head][dim % 8], so that every store
@@ -1405,7 +1327,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, bool fp8, hipStream_t stream
   if (fp8)
     hipLaunchKernelGGL(decode_split_f8_kernel, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_split_kernel<false>, dim3(a.G), dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(a.G), dim3(kDecThreads), 0, stream, a);
   return hipGetLastError();
 }
 
