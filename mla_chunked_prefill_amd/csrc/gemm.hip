@@ -55,6 +55,15 @@ constexpr int kGemmLdsB =
 static_assert(2 * kGemmLdsB <= 160 * 1024, "two workgroups per CU");
 static_assert(kGemmSlices >= kGemmStages, "pipeline depth");
 
+// the two 8-byte halves of a 16-byte chunk, exchanged when `swap`
+__device__ __forceinline__ uint4 half_swap(uint4 v, int swap) {
+  return swap ? make_uint4(v.z, v.w, v.x, v.y) : v;
+}
+// the two 4-byte words of each 8-byte half, exchanged when `swap`
+__device__ __forceinline__ uint4 word_swap(uint4 v, int swap) {
+  return swap ? make_uint4(v.y, v.x, v.w, v.z) : v;
+}
+
 // chunk permutation of a 64-byte operand row
 __device__ __forceinline__ int gswz(int r) { return (r >> 2) & 3; }
 
@@ -179,8 +188,13 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
   // registers 4q .. 4q + 3, i.e. four consecutive elements of the stored
   // dimension: one 8-byte LDS write (4 bytes for K in e4m3). 16-byte LDS
   // chunks are XORed by the line index so that the writes of 16 lines and the
-  // reads of one line spread over the banks. Rows of the chunk past nvalid
-  // are written as zeros, rows past max_rows are not written.
+  // reads of one line spread over the banks; in addition a line bit picks
+  // which 8-byte half of a chunk (and, for e4m3, which 4-byte word of a half)
+  // a lane writes, so that the 16 lanes an 8-byte write serves per cycle (32
+  // for 4-byte writes) hit distinct banks of the 128-byte bank cycle; the
+  // halves and words are put back in order after the 16-byte reads.
+  // Rows of the chunk past nvalid are written as zeros, rows past max_rows
+  // are not written.
   __syncthreads();  // every wave is done with the operand stages
   uint8_t* st = smem + wave * kGemmEpiB;
   const int row0 = m0 + wm;  // first latent row of the block
@@ -206,7 +220,7 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
               for (int e = 0; e < 4; ++e) x[e] = row0 + r + e < nvalid ? x[e] : 0.f;
             }
             const int chunk = (4 * i + q) ^ (line & 15);
-            *(uint2*)(st + line * 256 + chunk * 16 + 8 * hf) =
+            *(uint2*)(st + line * 256 + chunk * 16 + 8 * (hf ^ ((line >> 3) & 1))) =
                 make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
           } else {
             // line = latent row 32 i + l32; elements at d = 32 j + 8 q + 4 hf + e of the block
@@ -218,12 +232,13 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
             }
             if (kFp8K) {  // 64-byte lines
               const int chunk = (2 * j + (q >> 1)) ^ ((line >> 2) & 3);
-              *(uint32_t*)(st + line * 64 + chunk * 16 + 8 * (q & 1) + 4 * hf) =
+              *(uint32_t*)(st + line * 64 + chunk * 16 + 8 * ((q & 1) ^ ((line >> 4) & 1)) +
+                           4 * (hf ^ ((line >> 1) & 1))) =
                   f32_to_e4m3_sat(x[0]) | (f32_to_e4m3_sat(x[1]) << 8) |
                   (f32_to_e4m3_sat(x[2]) << 16) | (f32_to_e4m3_sat(x[3]) << 24);
             } else {  // 128-byte lines
               const int chunk = (4 * j + q) ^ ((line >> 1) & 7);
-              *(uint2*)(st + line * 128 + chunk * 16 + 8 * hf) =
+              *(uint2*)(st + line * 128 + chunk * 16 + 8 * (hf ^ (line & 1))) =
                   make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
             }
           }
@@ -241,7 +256,7 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
 #pragma unroll 4
       for (int it = 0; it < 16; ++it) {
         const int line = 4 * it + (lane >> 4);
-        const uint4 v = *(const uint4*)(st + line * 256 + ((cg ^ (line & 15)) * 16));
+        const uint4 v = half_swap(*(const uint4*)(st + line * 256 + ((cg ^ (line & 15)) * 16)), (line >> 3) & 1);
         *(uint4*)((uint8_t*)g.vt_out + (((size_t)h * kV + wn + line) * g.max_rows + row0) * 2 + cg * 16) = v;
       }
     }
@@ -251,7 +266,9 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
 #pragma unroll 4
     for (int it = 0; it < 8; ++it) {
       const int line = 16 * it + (lane >> 2);
-      const uint4 v = *(const uint4*)(st + line * 64 + ((cg ^ ((line >> 2) & 3)) * 16));
+      const uint4 v = word_swap(half_swap(*(const uint4*)(st + line * 64 + ((cg ^ ((line >> 2) & 3)) * 16)),
+                                          (line >> 4) & 1),
+                                (line >> 1) & 1);
       if (row0 + line < g.max_rows)
         *(uint4*)((uint8_t*)g.k_out + ((size_t)h * g.max_rows + row0 + line) * kNope + wn + cg * 16) = v;
     }
@@ -261,7 +278,7 @@ __device__ __forceinline__ void up_project_tile(const GemmArgs& g, uint8_t* smem
 #pragma unroll 4
     for (int it = 0; it < 16; ++it) {
       const int line = 8 * it + (lane >> 3);
-      const uint4 v = *(const uint4*)(st + line * 128 + ((cg ^ ((line >> 1) & 7)) * 16));
+      const uint4 v = half_swap(*(const uint4*)(st + line * 128 + ((cg ^ ((line >> 1) & 7)) * 16)), line & 1);
       if (row0 + line < g.max_rows)
         *(uint4*)((uint8_t*)g.k_out + (((size_t)h * g.max_rows + row0 + line) * kNope + wn) * 2 + cg * 16) = v;
     }
