@@ -695,8 +695,10 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
 //    2^(7 + kF8Slack) < 448 and a weight 2^-16 of the maximum's is still
 //    represented.
 //  - Rows keep their 16-byte chunks with the low two index bits XORed by
-//    zf8swz(row), which puts the score reads (16 rows at one chunk) and the
-//    transposed reads (16 rows x 32 bytes) on distinct bank groups.
+//    zf8swz(row) (bit 0: row bit 5, bit 1: row bit 2): the 16 lanes a score
+//    read serves per cycle (rows with 4 values of row % 4, bits 2 and 5
+//    varying) and the 32 lanes a transposed 8-byte read serves per cycle
+//    (8 rows, two chunks, both 8-byte halves) land on distinct banks.
 constexpr int kF8BN = 64;                              // keys per tile
 constexpr int kF8TileB = kF8BN * kCache;               // 36864 bytes
 constexpr int kF8TStages = 4;
@@ -713,7 +715,7 @@ typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 typedef int i32x2 __attribute__((__vector_size__(2 * sizeof(int))));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-__device__ __forceinline__ int zf8swz(int row) { return ((row >> 2) & 1) | (((row >> 5) & 1) << 1); }
+__device__ __forceinline__ int zf8swz(int row) { return ((row >> 5) & 1) | (((row >> 2) & 1) << 1); }
 __device__ __forceinline__ int zf8chunk(int row, int chunk) { return (chunk & ~3) | ((chunk & 3) ^ zf8swz(row)); }
 
 __device__ __forceinline__ u32x2 ds_read_tr8(const uint8_t* lds_byte_ptr) {
