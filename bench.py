@@ -211,7 +211,9 @@ def bench_prefill(args, binding, torch):
     from workloads import prefill_recipe
     from workloads.device import prefill_tensors
 
-    wl = prefill_recipe("dsv3_prefill_4k")
+    # chunk slots as the plan sizes them (one: the 4096-token prompt fits a
+    # 8192-token chunk); the parity tests also run the recipe's spare slot
+    wl = prefill_recipe("dsv3_prefill_4k", C=None)
     t = prefill_tensors(wl)
     B, H, T, C = wl.batch, wl.num_heads, wl.buffer_token_size, wl.max_chunks
     Tq = wl.total_q
@@ -775,7 +777,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q and latent cache, N(0,1/sqrt(512)) weights)",
         "config": {"workload": "dsv3_prefill_4k: batch 1, 4096 new tokens, no cache, "
                                "128 heads, q 192 = 128 nope + 64 rope, v 128, latent 512, "
-                               "page 128, buffer_token_size 8192, causal",
+                               "page 128, buffer_token_size 8192 (one chunk slot), causal",
                    "global_batch": 1, "seq_len": 4096, "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": "mfma",
