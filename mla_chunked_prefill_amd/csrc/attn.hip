@@ -43,6 +43,7 @@ namespace mla {
 
 constexpr int kAttnBM = 128;  // queries per workgroup
 constexpr int kAttnBN = 64;   // keys per tile
+constexpr int kAttnAhead = 4; // LDS operands read this many MFMAs ahead
 
 typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));  // 32 e4m3 values
 
@@ -310,15 +311,22 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
         }
       }
     } else {
+      // fragment i = 2 ks + mb, read kAttnAhead fragments ahead into rotating
+      // registers; the fences keep each read that far ahead of its MFMA
+      auto kload = [&](int i) __attribute__((always_inline)) {
+        const int ks = i >> 1, mb = i & 1;
+        const int off = ks < 8 ? nb[ks] + mb * 32 * L::kNopeRowB
+                               : rb[ks - 8] + mb * 32 * L::kRopeRowB;
+        return *(const bf16x8*)(st + off);
+      };
+      bf16x8 kf[kAttnAhead];
 #pragma unroll
-      for (int ks = 0; ks < 12; ++ks) {
+      for (int i = 0; i < kAttnAhead; ++i) kf[i] = kload(i);
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int off = ks < 8 ? nb[ks] + mb * 32 * L::kNopeRowB
-                                 : rb[ks - 8] + mb * 32 * L::kRopeRowB;
-          const bf16x8 ka = *(const bf16x8*)(st + off);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[mb], 0, 0, 0);
-        }
+      for (int i = 0; i < 24; ++i) {
+        s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kAttnAhead], qf[i >> 1], s[i & 1], 0, 0, 0);
+        if (i + kAttnAhead < 24) kf[i % kAttnAhead] = kload(i + kAttnAhead);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -353,32 +361,40 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(AttnArgs a) {
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float psum = 0.f;
-    bf16x8 pb[4];
+    // probabilities of 16-key step ks as the B operand of the value product:
+    // part j (0..3) forms keys 2 j, 2 j + 1 of each half-step's 8
+    uint32_t pw[4][4];
+    auto prob = [&](int ks, int j) __attribute__((always_inline)) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j], sl2, neg_m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j + 1], sl2, neg_m));
+      psum += p0 + p1;
+      pw[ks][j] = pack_bf16x2(p0, p1);
+    };
+    auto pbf = [&](int ks) __attribute__((always_inline)) {
+      return __builtin_bit_cast(bf16x8, u32x4{pw[ks][0], pw[ks][1], pw[ks][2], pw[ks][3]});
+    };
+
+    // ---- O^T += V^T P^T ----
+    // fragment i = 4 ks + md, read kAttnAhead fragments ahead; step ks + 1's
+    // probabilities are formed between step ks's MFMAs (the fences keep both)
+    auto vload = [&](int i) __attribute__((always_inline)) {
+      return *(const bf16x8*)(st + vb[i >> 2] + (i & 3) * 32 * L::kVRowB);
+    };
+    bf16x8 vf[kAttnAhead];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 w;
+    for (int i = 0; i < kAttnAhead; ++i) vf[i] = vload(i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j], sl2, neg_m));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[ks >> 1][(ks & 1) * 8 + 2 * j + 1], sl2, neg_m));
-        psum += p0 + p1;
-        w[j] = pack_bf16x2(p0, p1);
-      }
-      pb[ks] = __builtin_bit_cast(bf16x8, w);
+    for (int j = 0; j < 4; ++j) prob(0, j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      o[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i % kAttnAhead], pbf(i >> 2), o[i & 3], 0, 0, 0);
+      if (i + kAttnAhead < 16) vf[i % kAttnAhead] = vload(i + kAttnAhead);
+      if ((i >> 2) < 3) prob((i >> 2) + 1, i & 3);
+      __builtin_amdgcn_sched_barrier(0);
     }
     psum = sum_with_lane32(psum);
     l_run += psum;
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int md = 0; md < 4; ++md) {
-        const bf16x8 va = *(const bf16x8*)(st + vb[ks] + md * 32 * L::kVRowB);
-        o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], o[md], 0, 0, 0);
-      }
-    }
   };
 
   // q and the carry are in registers before any tile load is in flight, so
