@@ -342,7 +342,7 @@ int mla_decode(void* output, const void* q, const uint32_t* context_lengths,
  * workspace (mla_decode_workspace_size with the same arguments) exceeds it
  * is rejected with MLA_ERR_WORKSPACE before anything is enqueued; decode_b64's
  * shape (64 sequences, 128 heads, contexts to 32k, one partition per compute
- * unit) needs about 106 MiB. Every call on one GPU shares that GPU's array:
+ * unit) needs about 65 MiB. Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (on different streams, or from different
  * threads without ordering) race and give unspecified results. Nothing in
  * the array has to start at zero; a call leaves its contents behind. The

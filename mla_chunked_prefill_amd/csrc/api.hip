@@ -119,7 +119,7 @@ int decode_groups(int B, int max_ctx, int page_size, int num_partitions) {
 }
 
 // decode workspace: q_abs [B][H][576] bf16, cum [B+1] u32, wstart [G+1] u32,
-// wspan [B] int2, wfirst [G] i32, part_o [G+B][64][H][8] f32, part_ml [G+B][H][2] f32, o_lat
+// wspan [B] int2, wfirst [G] i32, part_o [G+B][64][H][8] bf16, part_ml [G+B][H][2] f32, o_lat
 // [B][H][2][512] bf16 (hi, lo). G split workgroups cover the batch's
 // concatenated contexts in equal ranges.
 struct DecodeWs {
@@ -128,7 +128,7 @@ struct DecodeWs {
   uint32_t* wstart;
   int2* wspan;
   int32_t* wfirst;
-  float* part_o;
+  uint16_t* part_o;
   float* part_ml;
   uint16_t* o_lat;
   int G;
@@ -150,8 +150,8 @@ DecodeWs decode_ws_layout(char* base, int B, int H, int max_ctx, int page_size,
   off = align_up(off + (size_t)B * sizeof(int2));
   w.wfirst = (int32_t*)(base + off);
   off = align_up(off + (size_t)w.G * sizeof(int32_t));
-  w.part_o = (float*)(base + off);
-  off = align_up(off + slots * H * mla::kLora * sizeof(float));
+  w.part_o = (uint16_t*)(base + off);
+  off = align_up(off + slots * H * mla::kLora * sizeof(uint16_t));
   w.part_ml = (float*)(base + off);
   off = align_up(off + slots * H * 2 * sizeof(float));
   w.o_lat = (uint16_t*)(base + off);

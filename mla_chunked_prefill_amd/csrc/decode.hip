@@ -637,21 +637,21 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_kernel(DecodeArgs
     }
     value_product(sZ + ((ntiles - 1) % kZStages) * kZStageB, pprev,
                   [&](int) __attribute__((always_inline)) {});
-    // partial state of (w, b): slot w + b. The output is stored by groups of
-    // eight dims, [slot][dim / 8][head][dim % 8], so that every store
-    // instruction writes 1 KB in one piece (32 heads x 32 bytes).
+    // partial state of (w, b): slot w + b. The output is stored in bf16 by
+    // groups of eight dims, [slot][dim / 8][head][dim % 8], so that every
+    // store instruction writes 512 bytes in one piece (32 heads x 16 bytes).
     if (hvalid) {
       const size_t base = ((size_t)(w + b) * a.H + head);
       // O^T register i of block md: dim 32 md + 8 (i / 4) + 4 hf + i % 4
-      float* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
+      uint16_t* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
 #pragma unroll
       for (int md = 0; md < 16; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
-          *(f32x4*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
+          u32x2 v;
+          v[0] = pack_bf16x2(o[md][g * 4 + 0], o[md][g * 4 + 1]);
+          v[1] = pack_bf16x2(o[md][g * 4 + 2], o[md][g * 4 + 3]);
+          *(u32x2*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
         }
       if (hf == 0) {
         // a wave whose scores outgrew the reference hands (exact maximum, -1)
@@ -1082,15 +1082,15 @@ __global__ void __launch_bounds__(kDecThreads, 1) decode_split_f8_kernel(DecodeA
     if (hvalid) {
       const size_t base = ((size_t)(w + b) * a.H + head);
       // O^T register i of block md: dim 32 md + 8 (i / 4) + 4 hf + i % 4
-      float* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
+      uint16_t* op = a.part_o + ((size_t)(w + b) * (kLora / 8) * a.H + head) * 8 + hf * 4;
 #pragma unroll
       for (int md = 0; md < 16; ++md)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 v;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = o[md][g * 4 + j];
-          *(f32x4*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
+          u32x2 v;
+          v[0] = pack_bf16x2(o[md][g * 4 + 0], o[md][g * 4 + 1]);
+          v[1] = pack_bf16x2(o[md][g * 4 + 2], o[md][g * 4 + 3]);
+          *(u32x2*)(op + (size_t)(4 * md + g) * a.H * 8) = v;
         }
       if (hf == 0) {
         a.part_ml[base * 2 + 0] = m_ref - kF8Bias;
@@ -1183,12 +1183,18 @@ __device__ void combine_head(const CombineArgs& c, int b, int h, int lane) {
         const int w = w0 + j;
         ok[j] = w <= span.y && c.wstart[w] < c.wstart[w + 1];
         const size_t base = (size_t)(w + b) * c.H + h;
-        const float* po = c.part_o + (((size_t)(w + b) * (kLora / 8) + lane) * c.H + h) * 8;
+        const uint16_t* po = c.part_o + (((size_t)(w + b) * (kLora / 8) + lane) * c.H + h) * 8;
         if (ok[j]) {
           m[j] = c.part_ml[base * 2];
           l[j] = c.part_ml[base * 2 + 1];
-          v0[j] = *(const f32x4*)(po);
-          v1[j] = *(const f32x4*)(po + 4);
+          const u32x4 pv = *(const u32x4*)(po);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            v0[j][2 * e] = bf16_lo(pv[e]);
+            v0[j][2 * e + 1] = bf16_hi(pv[e]);
+            v1[j][2 * e] = bf16_lo(pv[2 + e]);
+            v1[j][2 * e + 1] = bf16_hi(pv[2 + e]);
+          }
         }
       }
 #pragma unroll
@@ -1227,9 +1233,9 @@ __device__ void combine_head(const CombineArgs& c, int b, int h, int lane) {
 
 // Grid (B, ceil(H / 32), 4): a workgroup merges the partials of sequence b
 // for 32 heads and a quarter of the 512 dims. The partial outputs are stored
-// [slot][dim / 8][head][dim % 8], so lane (head = lane / 2, half = lane % 2)
-// of a wave reading one group of eight dims for 32 heads reads 1 KB in one
-// piece. First the per-head maximum over the partials (eight range lanes per
+// in bf16 [slot][dim / 8][head][dim % 8], so lane (head = lane / 2, half =
+// lane % 2) of a wave reading one group of eight dims for 32 heads reads
+// 512 bytes in one piece. First the per-head maximum over the partials (eight range lanes per
 // head, reduced through LDS); if any partial of these heads is marked, the
 // workgroup of quarter 0 merges them one head per wave with recomputation.
 __global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
@@ -1282,9 +1288,11 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
       const float m = ml[0], l = ml[1];
       f32x4 v[4];
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        v[gg] = *(const f32x4*)(c.part_o + ((slot * (kLora / 8) + g0 + gg) * c.H + head) * 8 +
-                                half * 4);
+      for (int gg = 0; gg < 4; ++gg) {
+        const u32x2 pv = *(const u32x2*)(c.part_o + ((slot * (kLora / 8) + g0 + gg) * c.H + head) * 8 +
+                                         half * 4);
+        v[gg] = f32x4{bf16_lo(pv[0]), bf16_hi(pv[0]), bf16_lo(pv[1]), bf16_hi(pv[1])};
+      }
       const float wt = __builtin_amdgcn_exp2f(m - Mh);
       L += wt * l;
 #pragma unroll

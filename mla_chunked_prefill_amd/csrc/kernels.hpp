@@ -65,14 +65,14 @@ struct DecodeArgs {
   const uint32_t* cum;       // [B+1] prefix sums of the context lengths
   const uint32_t* wstart;    // [G+1] first key of every key range
   const int32_t* wfirst;     // [G] first sequence every key range touches
-  float* part_o;             // [G + B][512 / 8][H][8]: dims by groups of 8
+  uint16_t* part_o;          // [G + B][512 / 8][H][8] bf16: dims by groups of 8
   float* part_ml;            // [G + B][H][2]
   int B, H, ps, maxp, num_pages, G;
   float scale_log2;
 };
 struct CombineArgs {
   uint16_t* o_lat;           // [B][H][2][512] bf16: hi then lo
-  float* part_o;             // [G + B][512 / 8][H][8]
+  const uint16_t* part_o;    // [G + B][512 / 8][H][8] bf16
   float* part_ml;            // [G + B][H][2] (max in the log2 domain, sum; a
                              // negative sum marks a partial to recompute)
   const uint32_t* cum;       // [B+1]
