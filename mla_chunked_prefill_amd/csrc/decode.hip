@@ -1281,24 +1281,45 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
     for (int e = 0; e < 4; ++e) acc[gg][e] = 0.f;
   if (span.y >= span.x) {
     float L = 0.f;
-    for (int w = span.x; w <= span.y; ++w) {
-      if (!(c.wstart[w] < c.wstart[w + 1])) continue;
-      const size_t slot = (size_t)(w + b);
-      const float* ml = c.part_ml + (slot * c.H + head) * 2;
-      const float m = ml[0], l = ml[1];
-      f32x4 v[4];
+    // eight ranges per round, every load of a round issued before any use (a
+    // sequence spans a handful of ranges, so most take one round)
+    constexpr int kBatch = 8;
+    for (int w0 = span.x; w0 <= span.y; w0 += kBatch) {
+      float m[kBatch], l[kBatch];
+      u32x2 pv[kBatch][4];
+      bool ok[kBatch];
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const u32x2 pv = *(const u32x2*)(c.part_o + ((slot * (kLora / 8) + g0 + gg) * c.H + head) * 8 +
-                                         half * 4);
-        v[gg] = f32x4{bf16_lo(pv[0]), bf16_hi(pv[0]), bf16_lo(pv[1]), bf16_hi(pv[1])};
+      for (int j = 0; j < kBatch; ++j) {
+        const int w = w0 + j;
+        // empty range: no partial (weight 0)
+        ok[j] = w <= span.y && c.wstart[w] < c.wstart[w + 1];
+        const size_t slot = (size_t)(w + b);
+        m[j] = 0.f;
+        l[j] = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) pv[j][gg] = u32x2{0u, 0u};
+        if (ok[j]) {
+          const float* ml = c.part_ml + (slot * c.H + head) * 2;
+          m[j] = ml[0];
+          l[j] = ml[1];
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            pv[j][gg] = *(const u32x2*)(c.part_o + ((slot * (kLora / 8) + g0 + gg) * c.H + head) * 8 +
+                                        half * 4);
+        }
       }
-      const float wt = __builtin_amdgcn_exp2f(m - Mh);
-      L += wt * l;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
+      for (int j = 0; j < kBatch; ++j) {
+        const float wt = ok[j] ? __builtin_amdgcn_exp2f(m[j] - Mh) : 0.f;
+        L += wt * l[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[gg][e] = fmaf(wt, v[gg][e], acc[gg][e]);
+        for (int gg = 0; gg < 4; ++gg) {
+          acc[gg][0] = fmaf(wt, bf16_lo(pv[j][gg][0]), acc[gg][0]);
+          acc[gg][1] = fmaf(wt, bf16_hi(pv[j][gg][0]), acc[gg][1]);
+          acc[gg][2] = fmaf(wt, bf16_lo(pv[j][gg][1]), acc[gg][2]);
+          acc[gg][3] = fmaf(wt, bf16_hi(pv[j][gg][1]), acc[gg][3]);
+        }
+      }
     }
     // a sink adds e^sink to the denominator (L and acc are relative to 2^Mh)
     if (c.sink) L += __builtin_amdgcn_exp2f(c.sink[b] * 1.44269504088896341f - Mh);

@@ -184,8 +184,12 @@ def test_up_project(B, H, R, n):
 # attention on given K/V (one chunk)
 # ---------------------------------------------------------------------------
 
-def test_prefill_attention_given_kv(B):
-    rng = np.random.default_rng(31)
+def _attention_given_kv(B, seed, fp8=False, plant=()):
+    """mla_prefill_attention on random K/V of one chunk (bf16, or e4m3 q,
+    K_nope and k_rope) against the oracle. plant: (sequence, key, query, head)
+    entries; that key's k_rope row becomes 20 * sign of that query's rope part
+    for that head, which lifts its logit about 100 log2 units above the rest."""
+    rng = np.random.default_rng(seed)
     H = 3
     new = np.array([5, 130, 64, 1, 200])
     cached = np.array([0, 70, 0, 300, 129])
@@ -195,25 +199,32 @@ def test_prefill_attention_given_kv(B):
     bro, co, bl = oracle.plan(offs, cached, T, 1)
     R = (int(bl[0]) + 63) // 64 * 64 + 64
     tq = int(offs[-1])
-    bits = lambda shape, s=1.0: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * s)
-    q_b = bits((tq, H, 192))
-    kn_b = bits((H, R, 128))
-    kr_b = bits((R, 64))
-    vt_b = bits((H, 128, R))
+    normal = lambda shape: rng.standard_normal(shape, dtype=np.float32)
+    if fp8:
+        enc, dec = f32_to_e4m3fn_codes, oracle.e4m3fn_to_f64
+        dev_k = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).cuda()
+    else:
+        enc, dec = f32_to_bf16_bits, oracle.bf16_to_f64
+        dev_k = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    q_b = enc(normal((tq, H, 192)))
+    kn_b = enc(normal((H, R, 128)))
+    kr_b = enc(normal((R, 64)))
+    vt_b = f32_to_bf16_bits(normal((H, 128, R)))
+    for b, key, qi, h in plant:
+        row = int(bro[0, b]) + key
+        kr_b[row] = enc(20.0 * np.sign(dec(q_b[offs[b] + qi, h, 128:])).astype(np.float32))
     out = torch.full((tq, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(B.mla_prefill_attention_workspace_size(len(new), tq, H), dtype=torch.uint8,
                      device="cuda")
     scale = 1 / math.sqrt(192)
-    B.mla_prefill_attention(out, dev(q_b), dev(kn_b), dev(vt_b), dev(kr_b), _u32(offs),
+    B.mla_prefill_attention(out, dev_k(q_b), dev_k(kn_b), dev(vt_b), dev_k(kr_b), _u32(offs),
                             _u32(cached), _u32(bro[0]), _u32(co[0]),
                             torch.tensor(bl, dtype=torch.int32, device="cuda"),
                             int(new.max()), scale, ws)
     torch.cuda.synchronize()
     got = _f64(out)
-    q = oracle.bf16_to_f64(q_b)
-    kn = oracle.bf16_to_f64(kn_b)
-    kr = oracle.bf16_to_f64(kr_b)
+    q, kn, kr = dec(q_b), dec(kn_b), dec(kr_b)
     vt = oracle.bf16_to_f64(vt_b)
     for b in range(len(new)):
         r0, r1 = int(bro[0, b]), int(bro[0, b + 1])
@@ -221,7 +232,31 @@ def test_prefill_attention_given_kv(B):
                                      kr[r0:r1], vt[:, :, r0:r1].transpose(2, 0, 1),
                                      cached[b] + np.arange(new[b]), np.arange(L[b]), scale, 128)
         err = np.abs(got[offs[b]:offs[b + 1]] - ref)
-        assert err.max() <= BF16_MAX and (err.size == 0 or err.mean() <= BF16_MEAN), (b, err.max())
+        if fp8:
+            assert err.max() <= FP8_MAX, (b, err.max())
+        else:
+            assert err.max() <= BF16_MAX and (err.size == 0 or err.mean() <= BF16_MEAN), (b, err.max())
+    return bro
+
+
+def test_prefill_attention_given_kv(B):
+    _attention_given_kv(B, 31)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_attention_planted_extreme_keys(B, fp8):
+    """Keys whose logits jump ~100 log2 units above the running maximum of the
+    queries that see them, in the first and in the second 32-key half of a
+    64-key tile and never in a sequence's first tile, so the softmax reference
+    must move and the accumulated output rescale by 2^-100 or so without
+    overflow. Sequence 4 starts at buffer row 570: its key 120 is row 690 (row
+    50 of the tile at 640), its key 200 row 770 (row 2 of the tile at 768);
+    sequence 1 starts at row 5: its key 133 is row 138 (row 10 of the tile at
+    128)."""
+    bro = _attention_given_kv(B, 32, fp8,
+                              plant=[(4, 120, 199, 0), (4, 200, 150, 2), (1, 133, 129, 1)])
+    # the rows sit where the docstring says (the plan is bit-exact on its own test)
+    assert int(bro[0, 4]) == 570 and int(bro[0, 1]) == 5
 
 
 # ---------------------------------------------------------------------------
