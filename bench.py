@@ -791,6 +791,9 @@ def main():
             "avg_launch_ms": round(p["attn_ms"], 4),
             "mfma_busy": None if mfma is None else mfma.get("mfma_busy"),
             "valu_per_mfma": None if mfma is None else mfma.get("valu_per_mfma"),
+            # the shader clock the counters saw (GRBM cycles over the kernel's
+            # duration): the 2.5 PFLOP/s peak assumes 2.4 GHz
+            "clock_ghz": None if mfma is None else mfma.get("clock_ghz"),
         },
         "prefill_breakdown_ms": {k: round(v, 4) for k, v in p["per_call_ms"].items()},
         "prefill_end_to_end_tflops": round((p["attn_flop"] + p["gemm_flop"]) /
