@@ -1281,8 +1281,8 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(CombineArgs c) {
     for (int e = 0; e < 4; ++e) acc[gg][e] = 0.f;
   if (span.y >= span.x) {
     float L = 0.f;
-    // eight ranges per pass, every load of a pass issued before any use (a
-    // sequence spans a handful of ranges, so most take one pass)
+    // eight ranges per round, every load of a round issued before any use (a
+    // sequence spans a handful of ranges, so most take one round)
     constexpr int kBatch = 8;
     for (int w0 = span.x; w0 <= span.y; w0 += kBatch) {
       float m[kBatch], l[kBatch];
