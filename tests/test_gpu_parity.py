@@ -732,9 +732,11 @@ def _sinks(vals):
     return torch.tensor(vals, dtype=torch.float32, device="cuda")
 
 
-def test_prefill_sinks_multichunk(B):
+@pytest.mark.parametrize("fp8", [False, True])
+def test_prefill_sinks_multichunk(B, fp8):
     # sequences split over several chunks: the sink enters once, at the end
-    wl = make_prefill("sink", 44, [70, 5, 140], [0, 60, 9], 2, 16, 64)
+    # (e4m3: the cache, q and the score path in e4m3, as the fp8 prefill runs)
+    wl = make_prefill("sink", 44, [70, 5, 140], [0, 60, 9], 2, 16, 64, fp8=fp8)
     sinks = [2.5, -np.inf, 0.3]
     t = prefill_tensors(wl)
     out = B.prefill(t["q"], t["input_row_offsets"], t["cache_lengths"], t["kv_cache"],
@@ -742,7 +744,11 @@ def test_prefill_sinks_multichunk(B):
                     wl.buffer_token_size, wl.max_chunks, int(wl.new_lens.max()), wl.scale,
                     wl.eps, attn_sink=_sinks(sinks))
     torch.cuda.synchronize()
-    _assert_close(_f64(out), oracle.prefill(wl, sinks=np.array(sinks)), BF16_MAX, BF16_MEAN)
+    ref = oracle.prefill(wl, sinks=np.array(sinks))
+    if fp8:
+        _assert_close(_f64(out), ref, FP8_MAX)
+    else:
+        _assert_close(_f64(out), ref, BF16_MAX, BF16_MEAN)
 
 
 @pytest.mark.parametrize("parts", [0, 3])
